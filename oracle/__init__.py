@@ -1,0 +1,162 @@
+"""fp64 CPU oracle for the LFM2 gated short causal convolution.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package; the product
+path (``gated_short_causal_amd``) never does, and the two share no code.
+
+Thin ctypes wrapper around ``liboracle.so`` (built from ``oracle.c`` by
+``oracle/build.py``).  Every function takes array-likes (numpy arrays, or CPU
+torch tensors of any float dtype, widened exactly to float64) and returns new
+float64 numpy arrays; inputs are never modified.  The arithmetic and the
+passages it follows are documented in ``oracle.h`` / ``oracle.c``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_ip = ctypes.POINTER(ctypes.c_int32)
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"oracle library missing: build it with `python oracle/build.py` ({_LIB_PATH})")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_set_threads.argtypes = [_int]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_get_threads.argtypes = []
+    lib.oracle_get_threads.restype = _int
+    lib.oracle_prefill.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _i64, _ip, _dp]
+    lib.oracle_decode.argtypes = [_int, _int, _int, _dp, _i64, _dp, _dp, _i64, _ip, _dp]
+    lib.oracle_verify.argtypes = [_int, _int, _int, _int, _dp, _i64, _dp, _dp, _i64, _ip, _dp, _dp]
+    lib.oracle_commit.argtypes = [_int, _int, _int, _int, _dp, _ip, _dp, _i64, _ip]
+    lib.oracle_backward.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _i64, _ip, _dp, _dp, _dp]
+    for name in ("oracle_prefill", "oracle_decode", "oracle_verify", "oracle_commit", "oracle_backward"):
+        getattr(lib, name).restype = _int
+    _lib = lib
+    return lib
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().oracle_get_threads())
+
+
+def f64(x):
+    """Exact widening to a C-contiguous float64 numpy array (None passes through)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: widen on the CPU (bf16 -> f64 is exact)
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def i32(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(a, t=_dp):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: arguments rejected by the oracle (rc={rc})")
+
+
+def _pool3(pool, H, K):
+    """Pool as a dense float64 [slots][H][K] copy (any [slots][>=H*K] layout accepted)."""
+    p = f64(pool)
+    p = p.reshape(p.shape[0], -1)[:, : H * K]
+    return np.ascontiguousarray(p).reshape(-1, H, K).copy()
+
+
+def prefill(inp, cu, w, pool=None, slot_idx=None):
+    """Ragged prefill.  Returns (y [total_T, H], new_pool or None)."""
+    inp, w, cu = f64(inp), f64(w), i32(cu)
+    H, K = w.shape
+    total_T = inp.shape[0]
+    N = cu.shape[0] - 1
+    y = np.full((total_T, H), np.nan)
+    newpool = None
+    sl = None
+    if pool is not None:
+        newpool = _pool3(pool, H, K)
+        sl = i32(slot_idx)
+    _check(_load().oracle_prefill(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w),
+                                  _p(newpool), 0 if newpool is None else newpool.shape[0],
+                                  _p(sl, _ip), _p(y)), "prefill")
+    return y, newpool
+
+
+def decode(inp, w, pool, slot_idx):
+    """One decode token per sequence (row i = sequence i).  Returns (y [N, H], new_pool)."""
+    inp, w = f64(inp), f64(w)
+    H, K = w.shape
+    sl = i32(slot_idx)
+    N = sl.shape[0]
+    newpool = _pool3(pool, H, K)
+    y = np.full((N, H), np.nan)
+    _check(_load().oracle_decode(H, K, N, _p(inp), inp.shape[1], _p(w), _p(newpool), newpool.shape[0],
+                                 _p(sl, _ip), _p(y)), "decode")
+    return y, newpool
+
+
+def verify(inp, w, pool, slot_idx, L):
+    """Verify window (row i*L+s).  Returns (y [N*L, H], tape [N, L, H, K]); pool untouched."""
+    inp, w = f64(inp), f64(w)
+    H, K = w.shape
+    sl = i32(slot_idx)
+    N = sl.shape[0]
+    p = _pool3(pool, H, K)
+    y = np.full((N * L, H), np.nan)
+    tape = np.full((N, L, H, K), np.nan)
+    _check(_load().oracle_verify(H, K, N, L, _p(inp), inp.shape[1], _p(w), _p(p), p.shape[0],
+                                 _p(sl, _ip), _p(tape), _p(y)), "verify")
+    return y, tape
+
+
+def commit(tape, accept, pool, slot_idx):
+    """Post-verify commit.  Returns the new pool [slots, H, K]."""
+    tape = f64(tape)
+    N, L, H, K = tape.shape
+    acc, sl = i32(accept), i32(slot_idx)
+    newpool = _pool3(pool, H, K)
+    _check(_load().oracle_commit(H, K, N, L, _p(tape), _p(acc, _ip), _p(newpool), newpool.shape[0],
+                                 _p(sl, _ip)), "commit")
+    return newpool
+
+
+def backward(inp, cu, w, dy, pool=None, slot_idx=None):
+    """Backward of prefill.  Returns (d_in [total_T, 3H] = dB|dC|dxv, dW [H, K])."""
+    inp, w, cu, dy = f64(inp), f64(w), i32(cu), f64(dy)
+    H, K = w.shape
+    total_T = inp.shape[0]
+    N = cu.shape[0] - 1
+    d_in = np.full((total_T, 3 * H), np.nan)
+    dW = np.full((H, K), np.nan)
+    p, sl = None, None
+    if pool is not None:
+        p = _pool3(pool, H, K)
+        sl = i32(slot_idx)
+    _check(_load().oracle_backward(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w),
+                                   _p(p), 0 if p is None else p.shape[0], _p(sl, _ip), _p(dy),
+                                   _p(d_in), _p(dW)), "backward")
+    return d_in, dW

@@ -1,0 +1,304 @@
+/*
+ * oracle.c -- fp64 CPU oracle for the LFM2 gated short causal convolution.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the test suite, the smoke check and the
+ * benchmark's CPU baseline, never by the product path.  Shares no code with
+ * the HIP library.  The definitions and the readings behind them are listed in
+ * oracle.h; each function below names the passage it follows.
+ *
+ * Style: plain loops over (sequence, channel, token), one output element at a
+ * time, in the order the definition states them.  OpenMP splits the channel
+ * loop only, so thread count never changes any result.
+ */
+#include "oracle.h"
+
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static int g_threads = 1;
+
+void oracle_set_threads(int n) {
+    if (n < 1) n = 1;
+#ifdef _OPENMP
+    g_threads = n;
+#else
+    g_threads = 1;
+#endif
+}
+
+int oracle_get_threads(void) { return g_threads; }
+
+/* Row-range sanity so that every access below stays in bounds. */
+static int check_cu(const int32_t* cu, int N, int64_t total_T) {
+    if (N < 0) return -1;
+    if (N == 0) return 0;
+    if (!cu || cu[0] < 0) return -1;
+    for (int i = 0; i < N; ++i)
+        if (cu[i + 1] < cu[i]) return -1;
+    if ((int64_t)cu[N] > total_T) return -1;
+    return 0;
+}
+
+static int check_slots(const int32_t* slot_idx, int N, int64_t num_slots) {
+    if (N > 0 && !slot_idx) return -1;
+    for (int i = 0; i < N; ++i)
+        if (slot_idx[i] < 0 || (int64_t)slot_idx[i] >= num_slots) return -1;
+    return 0;
+}
+
+/*
+ * Ragged prefill.
+ *
+ * MAX Pipelines LFM2 article, section "ShortConv implementation
+ * (LFM2ShortConv)": bx = b * xv from the three-way split of in_proj; the
+ * per-token loop shifts bx into the [H, K] state and takes
+ * conv_out = sum_k state * w, then y = c * conv_out.  Section "Batching and
+ * weight adaptation" / the graph inputs: tokens of all requests are packed
+ * with row offsets, and each conv layer receives one [H, K] state per request.
+ *
+ * The token loop is written here through the padded history of one channel,
+ *     X = [S0[0], ..., S0[K-1], bx[0], ..., bx[T-1]],
+ * in which the state after token t is X[t+1 .. t+K]; hence
+ *     conv[t] = sum_k w[k] * X[t+1+k]
+ * and the final state is X[T .. T+K-1].  (Decode and verify below use the
+ * shift form instead, so that the two codings can be checked against each
+ * other.)  All final states are written after all initial states are read.
+ */
+int oracle_prefill(int H, int K, int64_t total_T,
+                   const double* in, int64_t in_stride,
+                   const int32_t* cu, int N,
+                   const double* w,
+                   double* pool, int64_t num_slots, const int32_t* slot_idx,
+                   double* y) {
+    if (H <= 0 || K <= 0 || total_T < 0 || in_stride < 3 * (int64_t)H) return -1;
+    if (check_cu(cu, N, total_T)) return -1;
+    if (pool && check_slots(slot_idx, N, num_slots)) return -1;
+    if (N == 0) return 0;
+    if ((cu[N] > 0 && (!in || !y)) || !w) return -1;
+
+    const int64_t HK = (int64_t)H * K;
+    double* fin = NULL;
+    if (pool) {
+        fin = (double*)malloc(sizeof(double) * (size_t)N * (size_t)HK);
+        if (!fin) return -1;
+    }
+    int fail = 0;
+    for (int i = 0; i < N; ++i) {
+        const int64_t r0 = cu[i];
+        const int64_t T = (int64_t)cu[i + 1] - cu[i];
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            double* X = (double*)malloc(sizeof(double) * (size_t)(K + T));
+            if (!X) { fail = 1; continue; }
+            for (int k = 0; k < K; ++k)
+                X[k] = pool ? pool[(int64_t)slot_idx[i] * HK + (int64_t)h * K + k] : 0.0;
+            for (int64_t u = 0; u < T; ++u) {
+                const double* row = in + (r0 + u) * in_stride;
+                X[K + u] = row[h] * row[2 * H + h];              /* bx = B * xv */
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                const double* row = in + (r0 + t) * in_stride;
+                double conv = 0.0;
+                for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * X[t + 1 + k];
+                y[(r0 + t) * H + h] = row[H + h] * conv;        /* y = C * conv */
+            }
+            if (fin)
+                for (int k = 0; k < K; ++k) fin[(int64_t)i * HK + (int64_t)h * K + k] = X[T + k];
+            free(X);
+        }
+    }
+    if (fin) {
+        if (!fail)
+            for (int i = 0; i < N; ++i)
+                memcpy(pool + (int64_t)slot_idx[i] * HK, fin + (int64_t)i * HK, sizeof(double) * (size_t)HK);
+        free(fin);
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * One decode step per sequence.
+ *
+ * MAX Pipelines LFM2 article, section "ShortConv implementation
+ * (LFM2ShortConv)": the request's [H, K] state is taken from its slot, the
+ * oldest column is dropped and bx of the new token appended, conv_out is the
+ * tap-weighted sum of the new state, y = c * conv_out, and the new state goes
+ * back to the same slot (section "Inference state management").
+ */
+int oracle_decode(int H, int K, int N,
+                  const double* in, int64_t in_stride,
+                  const double* w,
+                  double* pool, int64_t num_slots, const int32_t* slot_idx,
+                  double* y) {
+    if (H <= 0 || K <= 0 || N < 0 || in_stride < 3 * (int64_t)H) return -1;
+    if (N == 0) return 0;
+    if (!in || !w || !pool || !y) return -1;
+    if (check_slots(slot_idx, N, num_slots)) return -1;
+    const int64_t HK = (int64_t)H * K;
+    int fail = 0;
+    for (int i = 0; i < N; ++i) {
+        const double* row = in + (int64_t)i * in_stride;
+        double* S_all = pool + (int64_t)slot_idx[i] * HK;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            double* S = S_all + (int64_t)h * K;
+            for (int k = 0; k + 1 < K; ++k) S[k] = S[k + 1];  /* drop the oldest */
+            S[K - 1] = row[h] * row[2 * H + h];                /* append bx      */
+            double conv = 0.0;
+            for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * S[k];
+            y[(int64_t)i * H + h] = row[H + h] * conv;
+        }
+    }
+    return fail;
+}
+
+/*
+ * Speculative verify window.
+ *
+ * SGLang PR 31041 summary, implementation item 2 and the shortconv_target_verify
+ * excerpt: the block of draft tokens of each request is run through the conv
+ * update from the request's slot state, and the conv window after every step
+ * is recorded in a tape indexed by batch row (the tape index buffer is
+ * arange(bs)), so that the state can later be rolled back to the accept
+ * boundary.  Reading: the slot pool itself is not written here.
+ */
+int oracle_verify(int H, int K, int N, int L,
+                  const double* in, int64_t in_stride,
+                  const double* w,
+                  const double* pool, int64_t num_slots, const int32_t* slot_idx,
+                  double* tape, double* y) {
+    if (H <= 0 || K <= 0 || N < 0 || L < 0 || in_stride < 3 * (int64_t)H) return -1;
+    if (N == 0 || L == 0) return 0;
+    if (!in || !w || !pool || !tape || !y) return -1;
+    if (check_slots(slot_idx, N, num_slots)) return -1;
+    const int64_t HK = (int64_t)H * K;
+    int fail = 0;
+    for (int i = 0; i < N; ++i) {
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            double S[64];
+            if (K > 64) { fail = 1; continue; }
+            for (int k = 0; k < K; ++k) S[k] = pool[(int64_t)slot_idx[i] * HK + (int64_t)h * K + k];
+            for (int s = 0; s < L; ++s) {
+                const int64_t r = (int64_t)i * L + s;
+                const double* row = in + r * in_stride;
+                for (int k = 0; k + 1 < K; ++k) S[k] = S[k + 1];
+                S[K - 1] = row[h] * row[2 * H + h];
+                double conv = 0.0;
+                for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * S[k];
+                y[r * H + h] = row[H + h] * conv;
+                for (int k = 0; k < K; ++k) tape[(r * H + h) * K + k] = S[k];
+            }
+        }
+    }
+    return fail ? -1 : 0;
+}
+
+/*
+ * Post-verify commit at the accept boundary.
+ *
+ * SGLang PR 31041 summary: the tape exists so the state can be rolled back to
+ * the accept boundary; the commit itself is the generic post-verify hybrid
+ * state commit (related PR 32828).  Reading: with accept length a, tokens
+ * 0..a-1 are kept, so the slot receives tape[i][a-1]; a = 0 keeps the state
+ * the slot already holds.
+ */
+int oracle_commit(int H, int K, int N, int L,
+                  const double* tape, const int32_t* accept,
+                  double* pool, int64_t num_slots, const int32_t* slot_idx) {
+    if (H <= 0 || K <= 0 || N < 0 || L < 0) return -1;
+    if (N == 0) return 0;
+    if (!accept || !pool) return -1;
+    if (check_slots(slot_idx, N, num_slots)) return -1;
+    for (int i = 0; i < N; ++i)
+        if (accept[i] < 0 || accept[i] > L) return -1;
+    const int64_t HK = (int64_t)H * K;
+    for (int i = 0; i < N; ++i) {
+        const int a = accept[i];
+        if (a == 0) continue;
+        if (!tape) return -1;
+        const double* src = tape + ((int64_t)i * L + (a - 1)) * HK;
+        memcpy(pool + (int64_t)slot_idx[i] * HK, src, sizeof(double) * (size_t)HK);
+    }
+    return 0;
+}
+
+/*
+ * Backward of the prefill forward.
+ *
+ * Liger-Kernel PR 1317, section "Kernel changes / Gated short convolution":
+ * the op's backward gives the input gradient through the fused B and C gates
+ * and a weight gradient with all K taps of a channel together.  The formulas
+ * are the derivatives of the forward definition (the pages print none).  With
+ * X the padded history used in oracle_prefill, for one channel of one sequence:
+ *     conv[t] = sum_k w[k] X[t+1+k],  y[t] = C[t] conv[t],  X[K+u] = B[u] xv[u]
+ * so, with g[t] = dy[t] C[t]:
+ *     dC[t]  = dy[t] conv[t]
+ *     dX[j]  = sum over (t, k) with t+1+k = j of w[k] g[t]
+ *     dBx[u] = dX[K+u] = sum_k w[k] g[u+K-1-k]     (terms with 0 <= u+K-1-k < T)
+ *     dB[u]  = dBx[u] xv[u],   dxv[u] = dBx[u] B[u]
+ *     dW[k]  = sum over sequences and t of g[t] X[t+1+k]
+ * No gradient is produced for the initial state.
+ */
+int oracle_backward(int H, int K, int64_t total_T,
+                    const double* in, int64_t in_stride,
+                    const int32_t* cu, int N,
+                    const double* w,
+                    const double* pool, int64_t num_slots, const int32_t* slot_idx,
+                    const double* dy,
+                    double* d_in, double* dW) {
+    if (H <= 0 || K <= 0 || total_T < 0 || in_stride < 3 * (int64_t)H) return -1;
+    if (check_cu(cu, N, total_T)) return -1;
+    if (pool && check_slots(slot_idx, N, num_slots)) return -1;
+    if (!w || !dW) return -1;
+    const int64_t HK = (int64_t)H * K;
+    int64_t maxT = 0;
+    for (int i = 0; i < N; ++i) {
+        const int64_t T = (int64_t)cu[i + 1] - cu[i];
+        if (T > maxT) maxT = T;
+    }
+    if (maxT > 0 && (!in || !dy || !d_in)) return -1;
+    int fail = 0;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int h = 0; h < H; ++h) {
+        double* X = (double*)malloc(sizeof(double) * (size_t)(K + maxT));
+        double* g = (double*)malloc(sizeof(double) * (size_t)(maxT > 0 ? maxT : 1));
+        if (!X || !g) { fail = 1; free(X); free(g); continue; }
+        for (int k = 0; k < K; ++k) dW[(int64_t)h * K + k] = 0.0;
+        for (int i = 0; i < N; ++i) {
+            const int64_t r0 = cu[i];
+            const int64_t T = (int64_t)cu[i + 1] - cu[i];
+            for (int k = 0; k < K; ++k)
+                X[k] = pool ? pool[(int64_t)slot_idx[i] * HK + (int64_t)h * K + k] : 0.0;
+            for (int64_t u = 0; u < T; ++u) {
+                const double* row = in + (r0 + u) * in_stride;
+                X[K + u] = row[h] * row[2 * H + h];
+            }
+            for (int64_t t = 0; t < T; ++t) {
+                const double* row = in + (r0 + t) * in_stride;
+                const double dyt = dy[(r0 + t) * H + h];
+                double conv = 0.0;
+                for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * X[t + 1 + k];
+                g[t] = dyt * row[H + h];
+                d_in[(r0 + t) * 3 * H + H + h] = dyt * conv;             /* dC */
+                for (int k = 0; k < K; ++k) dW[(int64_t)h * K + k] += g[t] * X[t + 1 + k];
+            }
+            for (int64_t u = 0; u < T; ++u) {
+                const double* row = in + (r0 + u) * in_stride;
+                double dbx = 0.0;
+                for (int k = 0; k < K; ++k) {
+                    const int64_t t = u + K - 1 - k;
+                    if (t >= 0 && t < T) dbx += w[(int64_t)h * K + k] * g[t];
+                }
+                d_in[(r0 + u) * 3 * H + h] = dbx * row[2 * H + h];          /* dB  */
+                d_in[(r0 + u) * 3 * H + 2 * H + h] = dbx * row[h];          /* dxv */
+            }
+        }
+        free(X);
+        free(g);
+    }
+    return fail ? -1 : 0;
+}
