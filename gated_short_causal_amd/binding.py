@@ -1,0 +1,157 @@
+"""Python binding of the C ABI: the same entry-point names, taking torch tensors.
+
+Argument marshalling only -- device pointers, strides, sizes and the current
+HIP stream are read from the tensors and handed to liblfm2sc.so; every step of
+the computation runs in the library's HIP kernels.  Outputs are caller-owned
+tensors, written in place, exactly as the C calls do.
+
+Tensor conventions (see include/lfm2sc.h for the full contract):
+  in_proj   [rows, >=3H]  bf16 or fp32, unit column stride (B | C | xv)
+  weight    [H, K]        same dtype, contiguous
+  state pool [slots, H, K] (or [slots, >=H*K]) same dtype, each slot contiguous
+  cu_seqlens, slot_idx, accept_len: int32 device tensors
+"""
+import torch
+
+from . import _lib
+
+LFM2SC_BF16 = 0
+LFM2SC_F32 = 1
+
+_DTYPES = {torch.bfloat16: LFM2SC_BF16, torch.float32: LFM2SC_F32}
+
+
+class Lfm2scError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        name = _lib.lib().lfm2sc_status_string(status).decode()
+        super().__init__(f"{name}: {detail}")
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Lfm2scError(rc, _lib.lib().lfm2sc_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+    return _DTYPES[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str):
+    """(row stride) of a 2-D row-major tensor with unit column stride."""
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride, got shape {tuple(t.shape)} strides {t.stride()}")
+    return t.stride(0)
+
+
+def _pool_stride(pool: torch.Tensor, H: int, K: int) -> int:
+    if pool.dim() == 3:
+        if pool.shape[1:] != (H, K) or pool.stride(2) != 1 or pool.stride(1) != K:
+            raise ValueError(f"state pool must be [slots, {H}, {K}] with contiguous slots")
+    elif pool.dim() == 2:
+        if pool.shape[1] < H * K or pool.stride(1) != 1:
+            raise ValueError(f"state pool must be [slots, >= {H * K}] with unit column stride")
+    else:
+        raise ValueError("state pool must be 2-D or 3-D")
+    return pool.stride(0)
+
+
+def _i32(t, name):
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _hk(weight: torch.Tensor):
+    if weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous [H, K] tensor")
+    return weight.shape[0], weight.shape[1]
+
+
+def lfm2sc_prefill_ragged(in_proj, cu_seqlens, weight, y, state_pool=None, slot_idx=None, bias=None):
+    H, K = _hk(weight)
+    _i32(cu_seqlens, "cu_seqlens"); _i32(slot_idx, "slot_idx")
+    num_slots = slot_stride = 0
+    if state_pool is not None:
+        slot_stride = _pool_stride(state_pool, H, K)
+        num_slots = state_pool.shape[0]
+    _check(_lib.lib().lfm2sc_prefill_ragged(
+        _dtype_code(weight), H, K, _ptr(in_proj), _rows(in_proj, "in_proj"), in_proj.shape[0],
+        _ptr(cu_seqlens), cu_seqlens.numel() - 1, _ptr(weight), _ptr(bias),
+        _ptr(state_pool), num_slots, slot_stride, _ptr(slot_idx),
+        _ptr(y), _rows(y, "y"), _stream(in_proj.device)))
+    return y
+
+
+def lfm2sc_decode_step(in_proj, weight, state_pool, slot_idx, y, bias=None):
+    H, K = _hk(weight)
+    _i32(slot_idx, "slot_idx")
+    _check(_lib.lib().lfm2sc_decode_step(
+        _dtype_code(weight), H, K, _ptr(in_proj), _rows(in_proj, "in_proj"), slot_idx.numel(),
+        _ptr(weight), _ptr(bias), _ptr(state_pool), state_pool.shape[0], _pool_stride(state_pool, H, K),
+        _ptr(slot_idx), _ptr(y), _rows(y, "y"), _stream(in_proj.device)))
+    return y
+
+
+def lfm2sc_verify_window(in_proj, weight, state_pool, slot_idx, L, windows, y, bias=None):
+    H, K = _hk(weight)
+    _i32(slot_idx, "slot_idx")
+    N = slot_idx.numel()
+    if windows is not None and (not windows.is_contiguous() or windows.numel() < N * L * H * K):
+        raise ValueError(f"windows must be a contiguous [{N}, {L}, {H}, {K}] tensor")
+    _check(_lib.lib().lfm2sc_verify_window(
+        _dtype_code(weight), H, K, _ptr(in_proj), _rows(in_proj, "in_proj"), N, L,
+        _ptr(weight), _ptr(bias), _ptr(state_pool), state_pool.shape[0], _pool_stride(state_pool, H, K),
+        _ptr(slot_idx), _ptr(windows), _ptr(y), _rows(y, "y"), _stream(in_proj.device)))
+    return y, windows
+
+
+def lfm2sc_commit_window(windows, accept_len, state_pool, slot_idx):
+    N, L, H, K = windows.shape
+    if not windows.is_contiguous():
+        raise ValueError("windows must be contiguous [N, L, H, K]")
+    _i32(accept_len, "accept_len"); _i32(slot_idx, "slot_idx")
+    _check(_lib.lib().lfm2sc_commit_window(
+        _dtype_code(windows), H, K, _ptr(windows), N, L, _ptr(accept_len),
+        _ptr(state_pool), state_pool.shape[0], _pool_stride(state_pool, H, K), _ptr(slot_idx),
+        _stream(windows.device)))
+    return state_pool
+
+
+def lfm2sc_backward_workspace_bytes(dtype, H, K, total_T, num_seqs) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.lib().lfm2sc_backward_workspace_bytes(code, H, K, total_T, num_seqs))
+
+
+def lfm2sc_backward(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, workspace,
+                    init_state_pool=None, slot_idx=None):
+    H, K = _hk(weight)
+    _i32(cu_seqlens, "cu_seqlens"); _i32(slot_idx, "slot_idx")
+    if dW.dtype != torch.float32 or not dW.is_contiguous():
+        raise TypeError("dW must be a contiguous float32 [H, K] tensor")
+    num_slots = slot_stride = 0
+    if init_state_pool is not None:
+        slot_stride = _pool_stride(init_state_pool, H, K)
+        num_slots = init_state_pool.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lib().lfm2sc_backward(
+        _dtype_code(weight), H, K, _ptr(in_proj), _rows(in_proj, "in_proj"), in_proj.shape[0],
+        _ptr(cu_seqlens), cu_seqlens.numel() - 1, _ptr(weight),
+        _ptr(init_state_pool), num_slots, slot_stride, _ptr(slot_idx),
+        _ptr(dy), _rows(dy, "dy"), _ptr(d_in_proj), _rows(d_in_proj, "d_in_proj"), _ptr(dW),
+        _ptr(workspace), ws_bytes, _stream(in_proj.device)))
+    return d_in_proj, dW
+
+
+def abi_version() -> int:
+    return int(_lib.lib().lfm2sc_abi_version())

@@ -1,0 +1,311 @@
+// bwd.hip -- ShortConv backward for gfx950: input gradients (dB, dC, dxv) and
+// the weight gradient dW, reduced deterministically in fp32.
+//
+// Derivatives of the forward (Liger-Kernel PR 1317, "Kernel changes / Gated
+// short convolution" describes a fused B/C-gate + conv input backward and a
+// weight backward that gathers all K taps of a channel; the formulas are ours,
+// from the forward definition).  Per channel of one sequence, with X the padded
+// history [state | bx...] and g = dy * C:
+//   dC[t]  = dy[t] * conv[t],            conv[t] = sum_k w[k] X[t+1+k]
+//   dbx[u] = sum_k w[k] g[u+K-1-k]       (g = 0 past the sequence end)
+//   dB[u]  = dbx[u] * xv[u],  dxv[u] = dbx[u] * B[u]
+//   dW[k]  = sum_t g[t] X[t+1+k]
+//
+// Pass structure (one read of dy and in_proj, one write of d_in): each lane
+// streams the tokens of its window in order.  At row r it forms g[r], bx[r],
+// conv[r] (from the K-1 bx values carried in registers), stores dC[r] and
+// accumulates dW; dbx needs the K-1 FUTURE g values, so dB/dxv are emitted
+// K-1 rows behind, at u = r-K+1, with B[u], xv[u] kept in a register FIFO.
+// The window re-reads K-1 rows behind it (B, xv: the halo) and K-1 rows
+// ahead of it (dy, C).  dW: each lane accumulates its 8 channels x K taps over
+// its window, the 4 waves of a workgroup are summed through LDS in a fixed
+// order, one fp32 partial row per workgroup window goes to the workspace,
+// and a second small kernel sums the rows in a fixed order.  No atomics, so
+// dW is bitwise reproducible.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lfm2sc {
+
+template <typename E, int K>
+struct BwdState {
+    static constexpr int KH = K > 1 ? K - 1 : 1;
+    float wf[kChPerLane][K];
+    float hist[kChPerLane][KH];   // X[r+1 .. r+K-1] for the current row r
+    float gw[kChPerLane][K];      // gw[c][a] = g[r-a]
+    Raw8<E> fb[KH], fx[KH];       // fb[a] = B of row r-1-a (same for xv)
+    float acc[kChPerLane][K];     // dW partial
+};
+
+// Row r of the window: all four operands loaded.  Emits dC[r] and, if `emit`,
+// dB/dxv of u = r-K+1.
+template <typename E, int K>
+__device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, const Raw8<E>& rb, const Raw8<E>& rc,
+                                        const Raw8<E>& rx, E* dc_p, bool emit, E* db_p, E* dxv_p) {
+    float dy[8], b[8], c[8], x[8], dC[8];
+    to_f32(rdy, dy); to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+        const float g = dy[ch] * c[ch];
+        const float bx = b[ch] * x[ch];
+        float conv = st.wf[ch][K - 1] * bx;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(st.wf[ch][k], st.hist[ch][k], conv);
+        dC[ch] = dy[ch] * conv;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) st.acc[ch][k] = fmaf(g, st.hist[ch][k], st.acc[ch][k]);
+        st.acc[ch][K - 1] = fmaf(g, bx, st.acc[ch][K - 1]);
+        if constexpr (K > 1) {
+#pragma unroll
+            for (int k = 0; k < K - 2; ++k) st.hist[ch][k] = st.hist[ch][k + 1];
+            st.hist[ch][K - 2] = bx;
+        }
+#pragma unroll
+        for (int a = K - 1; a > 0; --a) st.gw[ch][a] = st.gw[ch][a - 1];
+        st.gw[ch][0] = g;
+    }
+    store_f32x8<E>(dc_p, dC);
+    if (emit) {
+        float bu[8], xu[8];
+        if constexpr (K > 1) { to_f32(st.fb[K - 2], bu); to_f32(st.fx[K - 2], xu); }
+        else { to_f32(rb, bu); to_f32(rx, xu); }
+        float dB[8], dX[8];
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+            float dbx = st.wf[ch][0] * st.gw[ch][0];
+#pragma unroll
+            for (int k = 1; k < K; ++k) dbx = fmaf(st.wf[ch][k], st.gw[ch][k], dbx);
+            dB[ch] = dbx * xu[ch];
+            dX[ch] = dbx * bu[ch];
+        }
+        store_f32x8<E>(db_p, dB);
+        store_f32x8<E>(dxv_p, dX);
+    }
+    if constexpr (K > 1) {
+#pragma unroll
+        for (int a = K - 2; a > 0; --a) { st.fb[a] = st.fb[a - 1]; st.fx[a] = st.fx[a - 1]; }
+        st.fb[0] = rb; st.fx[0] = rx;
+    }
+}
+
+// Row r at or past the window end: only g[r] is needed (0 past the sequence
+// end); emits dB/dxv of u = r-K+1 when u is inside the window.
+template <typename E, int K>
+__device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const float* g, bool emit, E* db_p, E* dxv_p) {
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+#pragma unroll
+        for (int a = K - 1; a > 0; --a) st.gw[ch][a] = st.gw[ch][a - 1];
+        st.gw[ch][0] = g[ch];
+    }
+    if (emit) {
+        float bu[8], xu[8];
+        to_f32(st.fb[K - 2 >= 0 ? K - 2 : 0], bu);
+        to_f32(st.fx[K - 2 >= 0 ? K - 2 : 0], xu);
+        float dB[8], dX[8];
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+            float dbx = st.wf[ch][0] * st.gw[ch][0];
+#pragma unroll
+            for (int k = 1; k < K; ++k) dbx = fmaf(st.wf[ch][k], st.gw[ch][k], dbx);
+            dB[ch] = dbx * xu[ch];
+            dX[ch] = dbx * bu[ch];
+        }
+        store_f32x8<E>(db_p, dB);
+        store_f32x8<E>(dxv_p, dX);
+    }
+    if constexpr (K > 1) {
+#pragma unroll
+        for (int a = K - 2; a > 0; --a) { st.fb[a] = st.fb[a - 1]; st.fx[a] = st.fx[a - 1]; }
+    }
+}
+
+template <typename E, int K, int U>
+__device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSpan& sp, int ch0, BwdState<E, K>& st) {
+    const int H = a.H;
+    const int64_t lo = sp.lo, hi = sp.hi, T = sp.T, r0 = sp.r0;
+    const E* ib = a.in + ch0;
+    const E* gb = a.dy + ch0;
+    E* db = a.din + ch0;
+
+    // History X[lo+1 .. lo+K-1]: initial-state entries (index < K) or bx of
+    // earlier rows of this sequence.
+    if constexpr (K > 1) {
+        float s0[kChPerLane][K];
+        bool have_s0 = false;
+        if (lo < K - 1 && a.pool != nullptr) {
+            const int64_t slot = a.slot_idx[sp.seq];
+            if (slot_ok(slot, a.num_slots)) {
+                load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, s0);
+                have_s0 = true;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) {
+            const int64_t j = lo + 1 + k;
+            if (j < K) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) st.hist[c][k] = have_s0 ? s0[c][j] : 0.f;
+            } else {
+                const E* row = ib + (r0 + j - K) * a.in_stride;
+                float b[8], x[8];
+                load_f32x8<E>(row, b);
+                load_f32x8<E>(row + 2 * H, x);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) st.hist[c][k] = b[c] * x[c];
+            }
+        }
+    }
+
+    // Rows whose u = r-K+1 is still before the window: no dB/dxv emitted.
+    int64_t r = lo;
+    const int64_t head_end = (lo + K - 1 < hi) ? lo + K - 1 : hi;
+    for (; r < head_end; ++r) {
+        const E* row = ib + (r0 + r) * a.in_stride;
+        bwd_row<E, K>(st, ld8<E>(gb + (r0 + r) * a.dy_stride), ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H),
+                      db + (r0 + r) * a.din_stride + H, false, nullptr, nullptr);
+    }
+    // Steady state: U rows of loads in flight, then U rows of arithmetic.
+    for (; r + U <= hi; r += U) {
+        Raw8<E> rdy[U], rb[U], rc[U], rx[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const E* row = ib + (r0 + r + u) * a.in_stride;
+            rdy[u] = ld8<E>(gb + (r0 + r + u) * a.dy_stride);
+            rb[u] = ld8<E>(row);
+            rc[u] = ld8<E>(row + H);
+            rx[u] = ld8<E>(row + 2 * H);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t rr = r0 + r + u;
+            E* up = db + (rr - (K - 1)) * a.din_stride;
+            bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], db + rr * a.din_stride + H, true, up, up + 2 * H);
+        }
+    }
+    for (; r < hi; ++r) {
+        const int64_t rr = r0 + r;
+        const E* row = ib + rr * a.in_stride;
+        E* up = db + (rr - (K - 1)) * a.din_stride;
+        bwd_row<E, K>(st, ld8<E>(gb + rr * a.dy_stride), ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H),
+                      db + rr * a.din_stride + H, true, up, up + 2 * H);
+    }
+    // K-1 rows past the window: g only, from the next rows of the sequence.
+    if constexpr (K > 1) {
+        for (; r < hi + K - 1; ++r) {
+            float g[8];
+            if (r < T) {
+                float dyv[8], cv[8];
+                load_f32x8<E>(gb + (r0 + r) * a.dy_stride, dyv);
+                load_f32x8<E>(ib + (r0 + r) * a.in_stride + H, cv);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) g[c] = dyv[c] * cv[c];
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) g[c] = 0.f;
+            }
+            const int64_t u = r - (K - 1);
+            E* up = db + (r0 + u) * a.din_stride;
+            bwd_tail_row<E, K>(st, g, u >= lo, up, up + 2 * H);
+        }
+    }
+}
+
+template <typename E, int K, int U>
+__global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E> a) {
+    const int wave = wave_id();
+    const int lane = threadIdx.x % kWave;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int ch0 = (blockIdx.y * kWave + lane) * kChPerLane;
+    const bool lane_on = tile < a.ntiles && ch0 < a.H;
+
+    BwdState<E, K> st;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) { st.acc[c][k] = 0.f; st.gw[c][k] = 0.f; }
+
+    if (lane_on) {
+        const int64_t gap = (int64_t)a.sub * kWavesPerBlock;
+        const int64_t v0 = (int64_t)tile * gap + (int64_t)wave * a.sub;
+        SeqSpan sp;
+        if (find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) {
+            load_block<E, K>(a.w + (int64_t)ch0 * K, st.wf);
+            bwd_window<E, K, U>(a, sp, ch0, st);
+        }
+    }
+
+    // Sum the 4 waves' dW partials (same channels, consecutive windows).
+    __shared__ float red[kWavesPerBlock][kChPerLane * K][kWave];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) red[wave][c * K + k][lane] = st.acc[c][k];
+    __syncthreads();
+    if (wave == 0 && lane_on) {
+        float out[kChPerLane * K];
+#pragma unroll
+        for (int e = 0; e < kChPerLane * K; ++e)
+            out[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+        float4* dst = reinterpret_cast<float4*>(a.partial + (int64_t)tile * a.H * K + (int64_t)ch0 * K);
+#pragma unroll
+        for (int q = 0; q < 2 * K; ++q) dst[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+    }
+}
+
+// dW[j] = sum over windows of partial[window][j], j in [0, H*K): 32 columns x
+// 32 row groups per workgroup, then a fixed-order sum of the 32 row groups.
+constexpr int kFinCols = 32;
+constexpr int kFinRows = 32;
+
+__global__ __launch_bounds__(kFinCols * kFinRows) void dw_finish_kernel(const float* __restrict__ partial,
+                                                                       int64_t ntiles, int64_t HK, float* __restrict__ dW) {
+    const int col = threadIdx.x % kFinCols;
+    const int rg = threadIdx.x / kFinCols;
+    const int64_t j = (int64_t)blockIdx.x * kFinCols + col;
+    float s = 0.f;
+    if (j < HK) {
+#pragma unroll 8
+        for (int64_t r = rg; r < ntiles; r += kFinRows) s += partial[r * HK + j];
+    }
+    __shared__ float red[kFinRows][kFinCols + 1];
+    red[rg][col] = s;
+    __syncthreads();
+    if (rg == 0 && j < HK) {
+        float t = 0.f;
+#pragma unroll
+        for (int q = 0; q < kFinRows; ++q) t += red[q][col];
+        dW[j] = t;
+    }
+}
+
+template <typename E, int K>
+static hipError_t backward_k(const BackwardArgs<E>& a, hipStream_t s) {
+    if (a.ntiles > 0) {
+        const int gy = (a.H + kChPerWave - 1) / kChPerWave;
+        const int gx = pad_xcd(a.ntiles);
+        hipLaunchKernelGGL((backward_kernel<E, K, 4>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t HK = (int64_t)a.H * K;
+    hipLaunchKernelGGL(dw_finish_kernel, dim3((unsigned)((HK + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinRows), 0, s,
+                       (const float*)a.partial, (int64_t)a.ntiles, HK, a.dW);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_backward(const BackwardArgs<E>& a, int K, hipStream_t s) {
+    switch (K) {
+        case 1: return backward_k<E, 1>(a, s);
+        case 2: return backward_k<E, 2>(a, s);
+        case 3: return backward_k<E, 3>(a, s);
+        case 4: return backward_k<E, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template hipError_t launch_backward<uint16_t>(const BackwardArgs<uint16_t>&, int, hipStream_t);
+template hipError_t launch_backward<float>(const BackwardArgs<float>&, int, hipStream_t);
+
+}  // namespace lfm2sc

@@ -1,0 +1,176 @@
+// common.hpp -- shared device helpers for the ShortConv kernels (gfx950).
+//
+// Data layout used by every kernel:
+//   * a lane owns 8 consecutive channels, so every bf16 operand row segment it
+//     touches is one 16-byte access (fp32: two), and a 64-lane wave covers
+//     512 contiguous channels = 1 KiB (bf16) per operand per token row;
+//   * state entries of a lane's 8 channels are 8*K contiguous elements of the
+//     channel-major [H][K] slot block (48 bytes for bf16, K = 3), so pool
+//     traffic is already fully coalesced without any transpose;
+//   * values are widened to fp32 in registers and rounded once (RNE) when
+//     stored; gfx950 has a hardware packed fp32->bf16 RNE convert.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lfm2sc {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kChPerLane = 8;      // channels per lane
+constexpr int kChPerWave = kWave * kChPerLane;   // 512
+constexpr int kThreads = 256;      // 4 waves per workgroup
+constexpr int kWavesPerBlock = kThreads / kWave;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- element traits
+// uint16_t carries bf16 bit patterns; float is fp32.  Both expose 8-element
+// vector access on 16-byte aligned addresses.
+template <typename E> struct Elem;
+
+template <> struct Elem<uint16_t> {
+    static constexpr int kChunks = 1;   // 16-byte chunks per 8 elements
+    __device__ __forceinline__ static void unpack(const uint4& v, float* f) {
+        f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+        f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+        f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
+        f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
+    }
+    __device__ __forceinline__ static uint32_t pack2(float a, float b) {
+        f32x2 f = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+    }
+    __device__ __forceinline__ static uint4 pack(const float* f) {
+        uint4 v;
+        v.x = pack2(f[0], f[1]); v.y = pack2(f[2], f[3]);
+        v.z = pack2(f[4], f[5]); v.w = pack2(f[6], f[7]);
+        return v;
+    }
+};
+
+template <> struct Elem<float> {
+    static constexpr int kChunks = 2;
+    __device__ __forceinline__ static void unpack(const uint4* v, float* f) {
+        f[0] = __uint_as_float(v[0].x); f[1] = __uint_as_float(v[0].y);
+        f[2] = __uint_as_float(v[0].z); f[3] = __uint_as_float(v[0].w);
+        f[4] = __uint_as_float(v[1].x); f[5] = __uint_as_float(v[1].y);
+        f[6] = __uint_as_float(v[1].z); f[7] = __uint_as_float(v[1].w);
+    }
+};
+
+// Raw 8-element register image (kept packed until used to save VGPRs).
+template <typename E> struct Raw8 { uint4 c[Elem<E>::kChunks]; };
+
+template <typename E>
+__device__ __forceinline__ Raw8<E> ld8(const E* p) {
+    Raw8<E> r;
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) r.c[i] = q[i];
+    return r;
+}
+
+template <typename E>
+__device__ __forceinline__ void st8(E* p, const Raw8<E>& r) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) q[i] = r.c[i];
+}
+
+__device__ __forceinline__ void to_f32(const Raw8<uint16_t>& r, float* f) { Elem<uint16_t>::unpack(r.c[0], f); }
+__device__ __forceinline__ void to_f32(const Raw8<float>& r, float* f) { Elem<float>::unpack(r.c, f); }
+
+template <typename E> __device__ __forceinline__ Raw8<E> from_f32(const float* f);
+template <> __device__ __forceinline__ Raw8<uint16_t> from_f32<uint16_t>(const float* f) {
+    Raw8<uint16_t> r; r.c[0] = Elem<uint16_t>::pack(f); return r;
+}
+template <> __device__ __forceinline__ Raw8<float> from_f32<float>(const float* f) {
+    Raw8<float> r;
+    r.c[0] = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    r.c[1] = make_uint4(__float_as_uint(f[4]), __float_as_uint(f[5]), __float_as_uint(f[6]), __float_as_uint(f[7]));
+    return r;
+}
+
+template <typename E> __device__ __forceinline__ void load_f32x8(const E* p, float* f) { to_f32(ld8<E>(p), f); }
+template <typename E> __device__ __forceinline__ void store_f32x8(E* p, const float* f) { st8<E>(p, from_f32<E>(f)); }
+
+// 8*K contiguous elements (a lane's state block) <-> float s[8][K].
+template <typename E, int K>
+__device__ __forceinline__ void load_block(const E* p, float (&s)[kChPerLane][K]) {
+    float f[8 * K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) load_f32x8<E>(p + 8 * j, f + 8 * j);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) s[c][k] = f[c * K + k];
+}
+
+template <typename E, int K>
+__device__ __forceinline__ void store_block(E* p, const float (&s)[kChPerLane][K]) {
+    float f[8 * K];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) f[c * K + k] = s[c][k];
+#pragma unroll
+    for (int j = 0; j < K; ++j) store_f32x8<E>(p + 8 * j, f + 8 * j);
+}
+
+// Wave index inside the workgroup, as a wave-uniform (scalar) value so that
+// everything derived from it -- window bounds, row offsets, loop counts --
+// stays in SGPRs and addresses become scalar base + per-lane offset.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+// ---------------------------------------------------------------- XCD-aware block order
+// MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
+// with a private L2.  Remap so that XCD x receives a contiguous run of tiles:
+// neighbouring tiles share halo rows, which then hit in that XCD's L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
+    const int per = nblocks / kXcds;          // host pads nblocks to a multiple of 8
+    return (bid % kXcds) * per + bid / kXcds;
+}
+inline int pad_xcd(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
+
+// ---------------------------------------------------------------- ragged tiling
+// Packed sequences are laid on a virtual axis on which sequence i occupies
+// [cu[i] + i*gap, cu[i+1] + i*gap): consecutive sequences are separated by
+// `gap` empty positions, so any window of at most `gap` positions meets at
+// most one sequence.  Fixed-size windows of that axis are the work units; the
+// number of windows is bounded by ceil(total_T / gap) + N, known on the host
+// without reading cu_seqlens.  Row offsets are clamped to [0, total_T], so a
+// malformed cu_seqlens can produce wrong results but never an out-of-bounds
+// access.
+struct SeqSpan {
+    int seq;        // sequence index
+    int64_t r0;     // first packed row of the sequence
+    int64_t T;      // sequence length
+    int64_t lo, hi; // the window's part of the sequence, in sequence-local tokens
+};
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t a, int64_t b) { return v < a ? a : (v > b ? b : v); }
+
+__device__ __forceinline__ bool find_span(const int32_t* __restrict__ cu, int N, int64_t total_T, int64_t gap,
+                                          int64_t v0, int64_t v1, SeqSpan& s) {
+    int a = 0, b = N - 1, ans = -1;
+    while (a <= b) {
+        const int mid = (a + b) >> 1;
+        const int64_t vs = clamp64(cu[mid], 0, total_T) + (int64_t)mid * gap;
+        if (vs <= v1 - 1) { ans = mid; a = mid + 1; } else { b = mid - 1; }
+    }
+    if (ans < 0) return false;
+    const int64_t r0 = clamp64(cu[ans], 0, total_T);
+    const int64_t r1 = clamp64(cu[ans + 1], r0, total_T);
+    const int64_t vs = r0 + (int64_t)ans * gap;
+    s.seq = ans; s.r0 = r0; s.T = r1 - r0;
+    s.lo = v0 - vs > 0 ? v0 - vs : 0;
+    s.hi = v1 - vs < s.T ? v1 - vs : s.T;
+    return s.hi > s.lo;
+}
+
+__device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_slots) { return slot >= 0 && slot < num_slots; }
+
+}  // namespace lfm2sc

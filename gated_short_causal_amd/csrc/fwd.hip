@@ -1,0 +1,374 @@
+// fwd.hip -- forward ShortConv kernels for gfx950: ragged prefill, decode,
+// speculative verify window and post-verify commit.
+//
+// The op (MAX Pipelines LFM2 architecture article, "ShortConv implementation
+// (LFM2ShortConv)"): bx = B * xv; the [H, K] state drops its oldest column and
+// appends bx; conv = sum_k w[:, k] * state[:, k]; y = C * conv.
+//
+// All four kernels are HBM-streaming with a handful of FMAs per byte, so they
+// are written for memory-level parallelism: 16-byte accesses, several token
+// rows of loads issued before any arithmetic, no LDS and no barriers.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lfm2sc {
+
+// One token of one lane: bx = B*xv; conv over the K-1 history entries and bx;
+// y = C*conv; the history shifts by one.  hist[c][k] holds X[t+1+k] (k < K-1)
+// of the padded history X = [state | bx...] for the current token t.
+template <typename E, int K>
+__device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, const Raw8<E>& rx,
+                                          const float (&wf)[kChPerLane][K],
+                                          float (&hist)[kChPerLane][K > 1 ? K - 1 : 1], E* yp) {
+    float b[8], c[8], x[8], yv[8];
+    to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+        const float bx = b[ch] * x[ch];
+        float conv = wf[ch][K - 1] * bx;
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[ch][k], hist[ch][k], conv);
+        yv[ch] = c[ch] * conv;
+        if constexpr (K > 1) {
+#pragma unroll
+            for (int k = 0; k < K - 2; ++k) hist[ch][k] = hist[ch][k + 1];
+            hist[ch][K - 2] = bx;
+        }
+    }
+    store_f32x8<E>(yp, yv);
+}
+
+// ------------------------------------------------------------------ prefill
+// Work unit: one wave x one window of `sub` tokens x 512 channels.  A
+// workgroup is 4 consecutive windows of the virtual ragged axis (see
+// find_span), grid.y splits the channels.  Each lane streams its window's
+// tokens in order, carrying the K-1 previous bx values in registers (the
+// halo), so bx never reaches memory.
+//
+// In-place state update without a race: only the window holding a sequence's
+// token 0 (the "owner") reads the slot; it also handles tokens 0..K-2 (the
+// only ones that see the initial state) and writes the final state, which it
+// forms from the slot (for entries the sequence does not overwrite) and the
+// B, xv rows of the sequence's last K tokens.  No other wave touches the slot.
+template <typename E, int K, int U>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> a) {
+    const int wave = wave_id();
+    const int lane = threadIdx.x % kWave;
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    if (tile >= a.ntiles) return;
+    const int ch0 = (blockIdx.y * kWave + lane) * kChPerLane;
+    if (ch0 >= a.H) return;
+    const int64_t gap = (int64_t)a.sub * kWavesPerBlock;
+    const int64_t v0 = (int64_t)tile * gap + (int64_t)wave * a.sub;
+    SeqSpan sp;
+    if (!find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) return;
+    int64_t lo = sp.lo, hi = sp.hi;
+    const bool owner = (lo == 0);
+    if (owner) {
+        const int64_t m = (K - 1) < sp.T ? (K - 1) : sp.T;
+        if (hi < m) hi = m;
+    } else if (lo < K - 1) {
+        lo = K - 1;
+        if (lo >= hi) return;
+    }
+    const int H = a.H;
+    const E* base = a.in + ch0;
+
+    float wf[kChPerLane][K];
+    load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+
+    E* slotp = nullptr;
+    if (owner && a.pool != nullptr) {
+        const int64_t slot = a.slot_idx[sp.seq];
+        if (slot_ok(slot, a.num_slots)) slotp = a.pool + slot * a.slot_stride + (int64_t)ch0 * K;
+    }
+
+    float hist[kChPerLane][K > 1 ? K - 1 : 1];
+    if constexpr (K > 1) {
+        if (owner) {
+            float s0[kChPerLane][K];
+            if (slotp) {
+                load_block<E, K>(slotp, s0);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+#pragma unroll
+                    for (int k = 0; k < K; ++k) s0[c][k] = 0.f;
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) hist[c][k] = s0[c][k + 1];
+        } else {
+            // lo >= K-1: the K-1 tokens before lo are rows of this sequence.
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) {
+                const E* row = base + (sp.r0 + lo - (K - 1) + k) * a.in_stride;
+                float b[8], x[8];
+                load_f32x8<E>(row, b);
+                load_f32x8<E>(row + 2 * H, x);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) hist[c][k] = b[c] * x[c];
+            }
+        }
+    }
+
+    E* ybase = a.y + ch0;
+    int64_t t = lo;
+    for (; t + U <= hi; t += U) {
+        Raw8<E> rb[U], rc[U], rx[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const E* row = base + (sp.r0 + t + u) * a.in_stride;
+            rb[u] = ld8<E>(row);
+            rc[u] = ld8<E>(row + H);
+            rx[u] = ld8<E>(row + 2 * H);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, ybase + (sp.r0 + t + u) * a.y_stride);
+    }
+    for (; t < hi; ++t) {
+        const E* row = base + (sp.r0 + t) * a.in_stride;
+        fwd_token<E, K>(ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H), wf, hist,
+                        ybase + (sp.r0 + t) * a.y_stride);
+    }
+
+    if (slotp) {
+        // Final state = X[T .. T+K-1] of the padded history [state | bx...].
+        const int64_t T = sp.T;
+        float s0[kChPerLane][K];
+        if (T < K) load_block<E, K>(slotp, s0);
+        float fin[kChPerLane][K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t j = T + k;
+            if (j < K) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) fin[c][k] = s0[c][j];
+            } else {
+                const E* row = base + (sp.r0 + j - K) * a.in_stride;
+                float b[8], x[8];
+                load_f32x8<E>(row, b);
+                load_f32x8<E>(row + 2 * H, x);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) fin[c][k] = b[c] * x[c];
+            }
+        }
+        store_block<E, K>(slotp, fin);
+    }
+}
+
+// ------------------------------------------------------------------ decode
+// One token per sequence: grid.x = sequence, a lane = 8 channels.  Every load
+// of a lane is independent of the others except the state, whose address
+// needs the (wave-uniform, scalar-loaded) slot index.
+template <typename E, int K>
+__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs<E> a) {
+    const int i = blockIdx.x;
+    const int ch0 = (blockIdx.y * kThreads + threadIdx.x) * kChPerLane;
+    if (ch0 >= a.H) return;
+    const int H = a.H;
+    const int64_t slot = a.slot_idx[i];
+    const bool ok = slot_ok(slot, a.num_slots);
+    const E* row = a.in + (int64_t)i * a.in_stride + ch0;
+    const Raw8<E> rb = ld8<E>(row), rc = ld8<E>(row + H), rx = ld8<E>(row + 2 * H);
+    float wf[kChPerLane][K];
+    load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    E* sp = ok ? a.pool + slot * a.slot_stride + (int64_t)ch0 * K : nullptr;
+    float s[kChPerLane][K];
+    if (ok) {
+        load_block<E, K>(sp, s);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int k = 0; k < K; ++k) s[c][k] = 0.f;
+    }
+    float b[8], c8[8], x[8], yv[8];
+    to_f32(rb, b); to_f32(rc, c8); to_f32(rx, x);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
+        s[c][K - 1] = b[c] * x[c];
+        float conv = wf[c][K - 1] * s[c][K - 1];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
+        yv[c] = c8[c] * conv;
+    }
+    store_f32x8<E>(a.y + (int64_t)i * a.y_stride + ch0, yv);
+    if (ok) store_block<E, K>(sp, s);
+}
+
+// ------------------------------------------------------------------ verify
+// L draft tokens per sequence from the slot state (read only); after each
+// token the lane's 8 x K window goes to the tape windows[i][s].
+template <typename E, int K, int U>
+__global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs<E> a) {
+    const int i = blockIdx.x;
+    const int ch0 = (blockIdx.y * kThreads + threadIdx.x) * kChPerLane;
+    if (ch0 >= a.H) return;
+    const int H = a.H;
+    const int64_t HK = (int64_t)H * K;
+    const int64_t slot = a.slot_idx[i];
+    float wf[kChPerLane][K];
+    load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float s[kChPerLane][K];
+    if (slot_ok(slot, a.num_slots)) {
+        load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, s);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int k = 0; k < K; ++k) s[c][k] = 0.f;
+    }
+    const E* base = a.in + (int64_t)i * a.L * a.in_stride + ch0;
+    E* ybase = a.y + (int64_t)i * a.L * a.y_stride + ch0;
+    E* tbase = a.win + (int64_t)i * a.L * HK + (int64_t)ch0 * K;
+    int st = 0;
+    auto step = [&](const Raw8<E>& rb, const Raw8<E>& rc, const Raw8<E>& rx, int s_) {
+        float b[8], c8[8], x[8], yv[8];
+        to_f32(rb, b); to_f32(rc, c8); to_f32(rx, x);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
+            s[c][K - 1] = b[c] * x[c];
+            float conv = wf[c][K - 1] * s[c][K - 1];
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
+            yv[c] = c8[c] * conv;
+        }
+        store_f32x8<E>(ybase + (int64_t)s_ * a.y_stride, yv);
+        store_block<E, K>(tbase + (int64_t)s_ * HK, s);
+    };
+    for (; st + U <= a.L; st += U) {
+        Raw8<E> rb[U], rc[U], rx[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const E* row = base + (int64_t)(st + u) * a.in_stride;
+            rb[u] = ld8<E>(row); rc[u] = ld8<E>(row + H); rx[u] = ld8<E>(row + 2 * H);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) step(rb[u], rc[u], rx[u], st + u);
+    }
+    for (; st < a.L; ++st) {
+        const E* row = base + (int64_t)st * a.in_stride;
+        step(ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H), st);
+    }
+}
+
+// ------------------------------------------------------------------ commit
+// pool[slot[i]] <- windows[i][accept[i]-1] for accept[i] in [1, L]: a plain
+// 16-byte-per-lane copy of the accepted [H, K] window.
+template <typename E>
+__global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs<E> a, int64_t HK) {
+    const int i = blockIdx.x;
+    const int64_t e0 = ((int64_t)blockIdx.y * kThreads + threadIdx.x) * 8;
+    if (e0 >= HK) return;
+    const int acc = a.accept[i];
+    if (acc < 1 || acc > a.L) return;
+    const int64_t slot = a.slot_idx[i];
+    if (!slot_ok(slot, a.num_slots)) return;
+    const E* src = a.win + ((int64_t)i * a.L + (acc - 1)) * HK + e0;
+    st8<E>(a.pool + slot * a.slot_stride + e0, ld8<E>(src));
+}
+
+// ------------------------------------------------------------------ tiling policy
+// Window length per wave: long enough to amortise the K-1 halo rows, short
+// enough that the grid holds several waves per SIMD (1024 SIMDs on MI355X).
+static int pow2_floor(int64_t v) { int p = 1; while ((int64_t)p * 2 <= v) p *= 2; return p; }
+
+int prefill_sub(int64_t total_T, int H) {
+    const int64_t groups = (H + kChPerWave - 1) / kChPerWave;
+    const int64_t target_waves = 8192;
+    int64_t s = total_T * groups / target_waves;
+    int p = pow2_floor(s < 1 ? 1 : s);
+    if (p < 8) p = 8;
+    if (p > 64) p = 64;
+    return p;
+}
+
+int backward_sub(int64_t total_T, int H) { return prefill_sub(total_T, H); }
+
+int64_t ragged_tiles(int64_t total_T, int N, int sub) {
+    const int64_t gap = (int64_t)sub * kWavesPerBlock;
+    return (total_T + gap - 1) / gap + N;
+}
+
+// ------------------------------------------------------------------ launchers
+template <typename E, int K>
+static hipError_t prefill_k(const PrefillArgs<E>& a, hipStream_t s) {
+    const int gy = (a.H + kChPerWave - 1) / kChPerWave;
+    const int gx = pad_xcd(a.ntiles);
+    hipLaunchKernelGGL((prefill_kernel<E, K, 8>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_prefill(const PrefillArgs<E>& a, int K, hipStream_t s) {
+    switch (K) {
+        case 1: return prefill_k<E, 1>(a, s);
+        case 2: return prefill_k<E, 2>(a, s);
+        case 3: return prefill_k<E, 3>(a, s);
+        case 4: return prefill_k<E, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename E, int K>
+static hipError_t decode_k(const DecodeArgs<E>& a, hipStream_t s) {
+    const int lanes = a.H / kChPerLane;
+    hipLaunchKernelGGL((decode_kernel<E, K>), dim3(a.N, (lanes + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s) {
+    switch (K) {
+        case 1: return decode_k<E, 1>(a, s);
+        case 2: return decode_k<E, 2>(a, s);
+        case 3: return decode_k<E, 3>(a, s);
+        case 4: return decode_k<E, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename E, int K>
+static hipError_t verify_k(const VerifyArgs<E>& a, hipStream_t s) {
+    const int lanes = a.H / kChPerLane;
+    hipLaunchKernelGGL((verify_kernel<E, K, 4>), dim3(a.N, (lanes + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_verify(const VerifyArgs<E>& a, int K, hipStream_t s) {
+    switch (K) {
+        case 1: return verify_k<E, 1>(a, s);
+        case 2: return verify_k<E, 2>(a, s);
+        case 3: return verify_k<E, 3>(a, s);
+        case 4: return verify_k<E, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_commit(const CommitArgs<E>& a, int K, hipStream_t s) {
+    const int64_t HK = (int64_t)a.H * K;
+    const int64_t lanes = HK / 8;
+    hipLaunchKernelGGL((commit_kernel<E>), dim3(a.N, (unsigned)((lanes + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       a, HK);
+    return hipGetLastError();
+}
+
+template hipError_t launch_prefill<uint16_t>(const PrefillArgs<uint16_t>&, int, hipStream_t);
+template hipError_t launch_prefill<float>(const PrefillArgs<float>&, int, hipStream_t);
+template hipError_t launch_decode<uint16_t>(const DecodeArgs<uint16_t>&, int, hipStream_t);
+template hipError_t launch_decode<float>(const DecodeArgs<float>&, int, hipStream_t);
+template hipError_t launch_verify<uint16_t>(const VerifyArgs<uint16_t>&, int, hipStream_t);
+template hipError_t launch_verify<float>(const VerifyArgs<float>&, int, hipStream_t);
+template hipError_t launch_commit<uint16_t>(const CommitArgs<uint16_t>&, int, hipStream_t);
+template hipError_t launch_commit<float>(const CommitArgs<float>&, int, hipStream_t);
+
+}  // namespace lfm2sc

@@ -1,0 +1,82 @@
+// kernels.hpp -- argument blocks and launchers of the ShortConv kernels.
+// Host-side only declarations; definitions live in fwd.hip / bwd.hip / check.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lfm2sc {
+
+template <typename E>
+struct PrefillArgs {
+    const E* in; int64_t in_stride; int64_t total_T;
+    const int32_t* cu; int N;
+    const E* w;
+    E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    E* y; int64_t y_stride;
+    int H;
+    int sub;      // tokens per wave window (a workgroup window is 4 * sub)
+    int ntiles;   // number of workgroup windows
+};
+
+template <typename E>
+struct DecodeArgs {
+    const E* in; int64_t in_stride; int N;
+    const E* w;
+    E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    E* y; int64_t y_stride;
+    int H;
+};
+
+template <typename E>
+struct VerifyArgs {
+    const E* in; int64_t in_stride; int N; int L;
+    const E* w;
+    const E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    E* win;
+    E* y; int64_t y_stride;
+    int H;
+};
+
+template <typename E>
+struct CommitArgs {
+    const E* win; int N; int L; const int32_t* accept;
+    E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    int H;
+};
+
+template <typename E>
+struct BackwardArgs {
+    const E* in; int64_t in_stride; int64_t total_T;
+    const int32_t* cu; int N;
+    const E* w;
+    const E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    const E* dy; int64_t dy_stride;
+    E* din; int64_t din_stride;
+    float* partial;   // [ntiles][H*K] fp32 per-window dW sums
+    float* dW;        // [H][K]
+    int H;
+    int sub;
+    int ntiles;
+};
+
+// Tiling policy shared by the launchers and the workspace-size query.
+int prefill_sub(int64_t total_T, int H);
+int backward_sub(int64_t total_T, int H);
+int64_t ragged_tiles(int64_t total_T, int N, int sub);
+
+template <typename E> hipError_t launch_prefill(const PrefillArgs<E>& a, int K, hipStream_t s);
+template <typename E> hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s);
+template <typename E> hipError_t launch_verify(const VerifyArgs<E>& a, int K, hipStream_t s);
+template <typename E> hipError_t launch_commit(const CommitArgs<E>& a, int K, hipStream_t s);
+template <typename E> hipError_t launch_backward(const BackwardArgs<E>& a, int K, hipStream_t s);
+
+// Debug precondition checks (LFM2SC_CHECK=1).  Each returns 0 when the device
+// data satisfies the precondition, a nonzero mask otherwise; synchronises `s`.
+enum CheckBits { kBadSlotRange = 1, kDupSlot = 2, kBadCu = 4, kBadAccept = 8 };
+int check_device_preconditions(hipStream_t s, const int32_t* slot_idx, int N, int64_t num_slots,
+                               const int32_t* cu, int64_t total_T,
+                               const int32_t* accept, int L, hipError_t* err);
+
+}  // namespace lfm2sc

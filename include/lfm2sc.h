@@ -1,0 +1,225 @@
+/*
+ * lfm2sc.h -- C ABI of liblfm2sc.so: the LFM2 gated short causal convolution
+ * ("ShortConv") on AMD Instinct MI355X (gfx950).
+ *
+ * The op (MAX Pipelines LFM2 architecture article, section "ShortConv
+ * implementation (LFM2ShortConv)"): the in_proj output row of a token is split,
+ * in order, into three H-wide parts B, C and xv; bx = B * xv; a per-sequence
+ * state of K columns per channel (K = conv_L_cache, 3 for LFM2-1.2B) is
+ * advanced by dropping its oldest column and appending bx; the conv output is
+ * the tap-weighted sum of the state with weight [H, K] (the [H, 1, K] depthwise
+ * kernel with its unit axis dropped); y = C * conv; the new state is returned.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers unless stated otherwise; the caller
+ *    owns every buffer.  The library allocates no device memory, keeps no
+ *    device state between calls and is safe to call from several host threads.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
+ *    the null stream).  The return code covers host-side argument checks and
+ *    launch errors only; a fault inside a kernel surfaces at the caller's next
+ *    synchronisation.
+ *  - dtype: LFM2SC_BF16 or LFM2SC_F32.  It applies to the in_proj rows, the
+ *    weight, the state pool, y, the tape, dy and d_in alike.  Arithmetic is
+ *    fp32 in registers; each output element is rounded once (RNE) when stored.
+ *    In bf16 mode B*xv and dy*C are exact in fp32, so every stored state or
+ *    tape entry equals the exact value rounded to bf16.
+ *  - Layouts are row-major; every "stride" is in ELEMENTS between consecutive
+ *    rows.  in_proj rows hold B in columns [0, H), C in [H, 2H), xv in
+ *    [2H, 3H) (the split order b, c, xv of the ShortConv section above).
+ *  - The state pool is [num_slots][slot_stride] with slot s holding an [H][K]
+ *    block (channel-major, the K columns of a channel contiguous, oldest
+ *    first), i.e. the per-slot [1, hidden, conv_L_cache] buffer of the article's
+ *    section "Inference state management (ConvStateCache)".  Sequences name
+ *    their slot through slot_idx; slots must be distinct within a call and are
+ *    claimed and released by the caller (the library does no slot allocation).
+ *  - Requirements checked on the host: 8 <= H, H % 8 == 0; 1 <= K <= 4; every
+ *    device base pointer 16-byte aligned (dW: 4-byte); every stride a multiple
+ *    of 8 elements; in_stride >= 3H, y_stride >= H, dy_stride >= H,
+ *    din_stride >= 3H, slot_stride >= H*K.  A non-NULL bias is rejected with
+ *    LFM2SC_ERR_UNSUPPORTED in this version (the released LFM2 checkpoints are
+ *    bias-free, as the Liger-Kernel LFM2 PR notes under "Gated short
+ *    convolution").
+ *  - Device-side data (slot indices, row offsets, accept lengths) cannot be
+ *    checked on the host without a synchronisation.  Kernels never access
+ *    memory outside the buffers described by the size arguments: a slot index
+ *    outside [0, num_slots) makes that sequence skip every state read and write
+ *    (treated as a zero state, nothing written back); row offsets are clamped
+ *    to [0, total_T]; an accept length outside [0, L] commits nothing.  Set the
+ *    environment variable LFM2SC_CHECK=1 to have each call verify these
+ *    preconditions on the device, synchronise, and return
+ *    LFM2SC_ERR_PRECONDITION when one fails (slow; for debugging).
+ *  - Outputs must not overlap inputs.  Nothing is accumulated into an output:
+ *    y, tape, d_in and dW are overwritten.  Rows of y / d_in that belong to no
+ *    sequence (outside [cu_seqlens[0], cu_seqlens[N])) are not written.
+ */
+#ifndef LFM2SC_H
+#define LFM2SC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LFM2SC_ABI_VERSION 1
+
+enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
+
+enum lfm2sc_status {
+    LFM2SC_OK = 0,
+    LFM2SC_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                          */
+    LFM2SC_ERR_BAD_SHAPE = 2,      /* H, K, a count, a stride or a size is out of range   */
+    LFM2SC_ERR_ALIGNMENT = 3,      /* a pointer or stride breaks the alignment rules      */
+    LFM2SC_ERR_UNSUPPORTED = 4,    /* dtype, K or bias not supported by this version      */
+    LFM2SC_ERR_WORKSPACE = 5,      /* workspace NULL or smaller than required             */
+    LFM2SC_ERR_PRECONDITION = 6,   /* LFM2SC_CHECK=1 found bad device-side data           */
+    LFM2SC_ERR_HIP = 7             /* the HIP runtime reported an error at launch         */
+};
+
+/*
+ * Ragged (packed) prefill.
+ *
+ * Passage: MAX Pipelines LFM2 article, "ShortConv implementation
+ * (LFM2ShortConv)" (per-token state update, conv, C gate, new state) and
+ * "Batching and weight adaptation" / the graph's packed tokens with row
+ * offsets and one [H, K] state per request.
+ *
+ * in_proj    [total_T][in_stride]  packed rows of all sequences (B | C | xv).
+ * cu_seqlens [num_seqs+1] int32    sequence i owns rows [cu[i], cu[i+1]);
+ *                                  non-decreasing; cu[N] <= total_T.
+ * weight     [H][K].  bias: must be NULL.
+ * state_pool [num_slots][slot_stride] or NULL.  NULL: every sequence starts
+ *            from a zero state and no state is written (training forward).
+ *            Otherwise sequence i starts from pool[slot_idx[i]] and, in
+ *            place, that slot receives the last K columns of
+ *            [initial state | bx of the sequence's tokens] (a sequence of
+ *            length 0 leaves it unchanged, one shorter than K keeps part of the
+ *            old state).  Slots not named in slot_idx are never touched.
+ * slot_idx   [num_seqs] int32, distinct (ignored when state_pool is NULL).
+ * y          [total_T][y_stride]   y = C * conv.
+ * Packed sequences never share history: a sequence's first token sees only its
+ * own initial state (the hazard the InfiniLM LFM2 PR, "Notes for reviewers",
+ * avoids by rejecting packed prefill).
+ */
+int lfm2sc_prefill_ragged(int dtype, int H, int K,
+                          const void* in_proj, int64_t in_stride, int64_t total_T,
+                          const int32_t* cu_seqlens, int num_seqs,
+                          const void* weight, const void* bias,
+                          void* state_pool, int64_t num_slots, int64_t slot_stride,
+                          const int32_t* slot_idx,
+                          void* y, int64_t y_stride, void* stream);
+
+/*
+ * One decode token per sequence.
+ *
+ * Passage: MAX Pipelines LFM2 article, "ShortConv implementation" (take the
+ * request's [H, K] state, shift in bx, conv, gate, write the state back with a
+ * scatter by slot) and "Inference state management" (the slot pool).
+ *
+ * in_proj    [num_seqs][in_stride]  row i is the new token of sequence i.
+ * state_pool [num_slots][slot_stride] required; pool[slot_idx[i]] is advanced
+ *            in place by one token.  Slots not named are never touched.
+ * y          [num_seqs][y_stride].
+ */
+int lfm2sc_decode_step(int dtype, int H, int K,
+                       const void* in_proj, int64_t in_stride, int num_seqs,
+                       const void* weight, const void* bias,
+                       void* state_pool, int64_t num_slots, int64_t slot_stride,
+                       const int32_t* slot_idx,
+                       void* y, int64_t y_stride, void* stream);
+
+/*
+ * Speculative-decoding verify window.
+ *
+ * Passage: SGLang PR 31041 summary (DSpark speculative decoding for LFM2),
+ * implementation item 2 and its shortconv_target_verify excerpt: a block of L
+ * draft tokens per request is convolved from the request's slot state, and the
+ * conv window after every step is stored in a tape indexed by batch row so the
+ * state can be rolled back to the accept boundary; the tape is mandatory (the
+ * excerpt refuses to run without one).
+ *
+ * in_proj    [num_seqs*L][in_stride]  row i*L+s is draft token s of sequence i.
+ * state_pool read only: nothing is written to the pool by this call.
+ * windows    [num_seqs][L][H][K] (dense) required: windows[i][s] = the state of
+ *            sequence i after draft token s.  NULL -> LFM2SC_ERR_NULL_POINTER.
+ * y          [num_seqs*L][y_stride].
+ */
+int lfm2sc_verify_window(int dtype, int H, int K,
+                         const void* in_proj, int64_t in_stride, int num_seqs, int L,
+                         const void* weight, const void* bias,
+                         const void* state_pool, int64_t num_slots, int64_t slot_stride,
+                         const int32_t* slot_idx,
+                         void* windows,
+                         void* y, int64_t y_stride, void* stream);
+
+/*
+ * Post-verify commit (rollback to the accept boundary).
+ *
+ * Passage: SGLang PR 31041 summary, implementation item 2 (the tape exists for
+ * rollback at the accept boundary) and its related-work note on the generic
+ * post-verify hybrid-state commit.
+ *
+ * windows    [num_seqs][L][H][K] as written by lfm2sc_verify_window.
+ * accept_len [num_seqs] int32 in [0, L]: a > 0 copies windows[i][a-1] into
+ *            pool[slot_idx[i]] (tokens 0..a-1 kept); a == 0 leaves the slot.
+ */
+int lfm2sc_commit_window(int dtype, int H, int K,
+                         const void* windows, int num_seqs, int L,
+                         const int32_t* accept_len,
+                         void* state_pool, int64_t num_slots, int64_t slot_stride,
+                         const int32_t* slot_idx, void* stream);
+
+/*
+ * Bytes of device workspace lfm2sc_backward needs for these sizes (it holds
+ * per-tile fp32 partial sums of dW).  Returns 0 for invalid sizes.
+ */
+size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T, int num_seqs);
+
+/*
+ * Backward of lfm2sc_prefill_ragged (training).
+ *
+ * Passage: Liger-Kernel PR 1317 ("Add LFM2, LFM2-MoE, and LFM2-VL support"),
+ * "Kernel changes / Gated short convolution": gradients through both gates and
+ * the conv input, and a weight gradient that gathers all K taps of a channel.
+ * The formulas are the derivatives of the forward: with g = dy*C,
+ *   dC = dy * conv;  dbx[u] = sum_k w[k] g[u+K-1-k] (inside the sequence);
+ *   dB = dbx * xv;   dxv = dbx * B;   dW[h][k] = sum over tokens of g * (the
+ *   state entry k that multiplied w[h][k]).
+ *
+ * in_proj, cu_seqlens, weight: as for the forward call.
+ * init_state_pool / num_slots / slot_stride / slot_idx: the initial states the
+ *            forward started from (read only); NULL pool = zero states.  No
+ *            gradient is returned for them.
+ * dy         [total_T][dy_stride].
+ * d_in_proj  [total_T][din_stride]  columns dB | dC | dxv (overwritten).
+ * dW         [H][K] fp32 (overwritten; reduced over all sequences and tokens
+ *            in a fixed order, so results are bitwise reproducible).
+ * workspace  device buffer of at least lfm2sc_backward_workspace_bytes(...)
+ *            bytes, 16-byte aligned; contents on entry are ignored.
+ */
+int lfm2sc_backward(int dtype, int H, int K,
+                    const void* in_proj, int64_t in_stride, int64_t total_T,
+                    const int32_t* cu_seqlens, int num_seqs,
+                    const void* weight,
+                    const void* init_state_pool, int64_t num_slots, int64_t slot_stride,
+                    const int32_t* slot_idx,
+                    const void* dy, int64_t dy_stride,
+                    void* d_in_proj, int64_t din_stride,
+                    float* dW,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* lfm2sc_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* lfm2sc_last_error(void);
+
+/* LFM2SC_ABI_VERSION of the loaded library. */
+int lfm2sc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LFM2SC_H */

@@ -1,0 +1,181 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Every call below is built to fail host validation (or to hit an early no-work
+return), so none of them reaches a kernel launch: the pointers are fake.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_short_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lfm2sc.h")
+
+OK, NULLP, SHAPE, ALIGN, UNSUP, WS, PRECOND, HIP = range(8)
+
+P = 0x10000      # fake, 16-byte aligned "device" address (never dereferenced)
+MIS = 0x10002    # fake, misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(lfm2sc_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) == 9, names
+    assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define\s+LFM2SC_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert L.lfm2sc_abi_version() == int(m.group(1))
+
+
+def test_status_strings(L):
+    names = ["LFM2SC_OK", "LFM2SC_ERR_NULL_POINTER", "LFM2SC_ERR_BAD_SHAPE", "LFM2SC_ERR_ALIGNMENT",
+             "LFM2SC_ERR_UNSUPPORTED", "LFM2SC_ERR_WORKSPACE", "LFM2SC_ERR_PRECONDITION", "LFM2SC_ERR_HIP"]
+    for code, name in enumerate(names):
+        assert L.lfm2sc_status_string(code).decode() == name
+    assert L.lfm2sc_status_string(99).decode() == "LFM2SC_UNKNOWN_STATUS"
+
+
+def _prefill(L, **kw):
+    a = dict(dtype=0, H=256, K=3, in_proj=P, in_stride=768, total_T=64, cu=P, N=1, w=P, bias=None,
+             pool=None, num_slots=0, slot_stride=0, slot_idx=None, y=P, y_stride=256, stream=None)
+    a.update(kw)
+    return L.lfm2sc_prefill_ragged(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["total_T"], a["cu"],
+                                   a["N"], a["w"], a["bias"], a["pool"], a["num_slots"], a["slot_stride"],
+                                   a["slot_idx"], a["y"], a["y_stride"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), UNSUP), (dict(H=0), SHAPE), (dict(H=12), SHAPE), (dict(H=4), SHAPE),
+    (dict(K=0), UNSUP), (dict(K=5), UNSUP), (dict(bias=P), UNSUP),
+    (dict(N=-1), SHAPE), (dict(total_T=-1), SHAPE), (dict(total_T=1 << 31), SHAPE),
+    (dict(in_stride=700), SHAPE), (dict(in_stride=772), ALIGN), (dict(y_stride=100), SHAPE), (dict(y_stride=260), ALIGN),
+    (dict(in_proj=None), NULLP), (dict(cu=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
+    (dict(in_proj=MIS), ALIGN), (dict(w=MIS), ALIGN), (dict(y=MIS), ALIGN), (dict(cu=P + 2), ALIGN),
+    (dict(pool=P, num_slots=4, slot_stride=768, slot_idx=None), NULLP),
+    (dict(pool=P, num_slots=0, slot_stride=768, slot_idx=P), SHAPE),
+    (dict(pool=P, num_slots=4, slot_stride=760, slot_idx=P), SHAPE),
+    (dict(pool=P, num_slots=4, slot_stride=772, slot_idx=P), ALIGN),
+    (dict(pool=MIS, num_slots=4, slot_stride=768, slot_idx=P), ALIGN),
+])
+def test_prefill_rejects(L, kw, code):
+    assert _prefill(L, **kw) == code
+    assert L.lfm2sc_last_error().decode().startswith("lfm2sc_prefill_ragged")
+
+
+def test_prefill_no_work_is_ok_without_launch(L):
+    # no sequence, or no token: returns OK before touching any pointer
+    assert _prefill(L, N=0, in_proj=None, cu=None, y=None) == OK
+    assert _prefill(L, total_T=0, in_proj=None, cu=None, y=None) == OK
+    assert L.lfm2sc_last_error().decode() == ""
+
+
+def _decode(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, N=256, w=P, bias=None, pool=P, num_slots=1024,
+             slot_stride=6144, slot_idx=P, y=P, y_stride=2048, stream=None)
+    a.update(kw)
+    return L.lfm2sc_decode_step(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["N"], a["w"], a["bias"],
+                                a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"], a["y"], a["y_stride"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pool=None), NULLP), (dict(slot_idx=None), NULLP), (dict(y=None), NULLP), (dict(in_proj=None), NULLP),
+    (dict(N=-3), SHAPE), (dict(num_slots=0), SHAPE), (dict(slot_stride=6136), SHAPE), (dict(dtype=7), UNSUP),
+    (dict(bias=P), UNSUP), (dict(in_stride=6148), ALIGN), (dict(pool=MIS), ALIGN), (dict(slot_idx=P + 1), ALIGN),
+])
+def test_decode_rejects(L, kw, code):
+    assert _decode(L, **kw) == code
+
+
+def _verify(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, N=64, Lb=8, w=P, bias=None, pool=P, num_slots=256,
+             slot_stride=6144, slot_idx=P, win=P, y=P, y_stride=2048, stream=None)
+    a.update(kw)
+    return L.lfm2sc_verify_window(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["N"], a["Lb"], a["w"],
+                                  a["bias"], a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"], a["win"],
+                                  a["y"], a["y_stride"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(win=None), NULLP), (dict(win=None, N=0), NULLP),   # the tape is mandatory, even for an empty batch
+    (dict(win=MIS), ALIGN), (dict(Lb=-1), SHAPE), (dict(pool=None), NULLP), (dict(K=9), UNSUP),
+])
+def test_verify_rejects(L, kw, code):
+    assert _verify(L, **kw) == code
+
+
+def _commit(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, win=P, N=64, Lb=8, acc=P, pool=P, num_slots=256, slot_stride=6144, slot_idx=P,
+             stream=None)
+    a.update(kw)
+    return L.lfm2sc_commit_window(a["dtype"], a["H"], a["K"], a["win"], a["N"], a["Lb"], a["acc"], a["pool"],
+                                  a["num_slots"], a["slot_stride"], a["slot_idx"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(win=None), NULLP), (dict(acc=None), NULLP), (dict(pool=None), NULLP), (dict(slot_idx=None), NULLP),
+    (dict(N=-1), SHAPE), (dict(acc=P + 2), ALIGN), (dict(H=7), SHAPE),
+])
+def test_commit_rejects(L, kw, code):
+    assert _commit(L, **kw) == code
+
+
+def test_commit_no_work(L):
+    assert _commit(L, N=0, win=None, acc=None, pool=None, slot_idx=None) == OK
+    assert _commit(L, Lb=0, win=None, acc=None) == OK
+
+
+def _bwd(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, total_T=4096, cu=P, N=1, w=P, pool=None, num_slots=0,
+             slot_stride=0, slot_idx=None, dy=P, dy_stride=2048, din=P, din_stride=6144, dW=P, ws=P, ws_bytes=1 << 30,
+             stream=None)
+    a.update(kw)
+    return L.lfm2sc_backward(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["total_T"], a["cu"], a["N"],
+                             a["w"], a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"], a["dy"],
+                             a["dy_stride"], a["din"], a["din_stride"], a["dW"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dW=None), NULLP), (dict(dW=P + 2), ALIGN), (dict(dy=None), NULLP), (dict(din=None), NULLP),
+    (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=P + 8), ALIGN), (dict(din_stride=6000), SHAPE),
+    (dict(dy_stride=2044), SHAPE), (dict(dy_stride=2052), ALIGN), (dict(cu=None), NULLP),
+    (dict(pool=P, num_slots=2, slot_stride=6144, slot_idx=None), NULLP), (dict(K=0), UNSUP),
+])
+def test_backward_rejects(L, kw, code):
+    assert _bwd(L, **kw) == code
+
+
+def test_workspace_bytes(L):
+    f = L.lfm2sc_backward_workspace_bytes
+    assert f(0, 2048, 3, 0, 0) == 0
+    assert f(0, 2048, 3, 65536, 1) > 0
+    assert f(0, 2048, 3, 65536, 1) % 256 == 0
+    # partial rows of H*K fp32 values: grows with tokens and with sequences
+    assert f(0, 2048, 3, 65536, 1) >= 2048 * 3 * 4
+    assert f(0, 2048, 3, 65536, 8) >= f(0, 2048, 3, 65536, 1)
+    assert f(0, 2048, 3, 1 << 20, 1) > f(0, 2048, 3, 65536, 1)
+    assert f(9, 2048, 3, 64, 1) == 0 and f(0, 12, 3, 64, 1) == 0 and f(0, 2048, 5, 64, 1) == 0
+
+
+def test_binding_names_match_c_abi():
+    import gated_short_causal_amd as g
+    for n in ("lfm2sc_prefill_ragged", "lfm2sc_decode_step", "lfm2sc_verify_window", "lfm2sc_commit_window",
+              "lfm2sc_backward", "lfm2sc_backward_workspace_bytes"):
+        assert callable(getattr(g, n)) and n in _lib.SIGNATURES
