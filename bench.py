@@ -1,0 +1,284 @@
+"""Benchmark of the LFM2 ShortConv hot path on one MI355X.
+
+A step is one pass of the whole training hot path over one batch of seeded
+synthetic input: lfm2sc_prefill_ragged (forward: B*xv, causal depthwise conv,
+C gate) followed by lfm2sc_backward (dB, dC, dxv and the deterministic dW
+reduction), on one sequence of T=65536 tokens, H=2048, K=3, bf16 I/O with fp32
+accumulation, zero initial state.  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  `value` is the step's algorithmic HBM bytes divided by
+the measured step time (GB/s); the roofline object reports the backward call
+(its dominant launch) against the MI355X HBM peak; cpu_baseline times the fp64
+oracle on a bounded channel sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+       python bench.py --calibrate-copy   (plain device copy of known size, for counter scaling)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD public specification
+METRIC = "ShortConv GB/s and % of HBM peak; fwd+bwd ms at T=65536, H=2048, K=3"
+
+
+def algo_bytes_fwd(T, H, K, e):
+    """Forward: read B, C, xv (3H) and write y (H) per token, plus the weight."""
+    return T * 4 * H * e + H * K * e
+
+
+def algo_bytes_bwd(T, H, K, e):
+    """Backward: read dy (H) and B, C, xv (3H), write dB, dC, dxv (3H) per token, plus weight and fp32 dW."""
+    return T * 7 * H * e + H * K * e + H * K * 4
+
+
+def algo_bytes_decode(N, H, K, e):
+    """Per sequence: read B, C, xv and the [H,K] state, write y and the state; plus weight and slot ids."""
+    return N * (3 * H * e + H * e + 2 * H * K * e) + H * K * e + 4 * N
+
+
+def algo_bytes_prefill(total_T, N, H, K, e):
+    """Read in_proj (3H), write y (H) per token; read + write each sequence's state; weight; offsets and slots."""
+    return total_T * 4 * H * e + N * 2 * H * K * e + H * K * e + 4 * (2 * N + 1)
+
+
+def algo_bytes_verify(N, L, H, K, e):
+    """Read in_proj rows and the states, write y and the per-step tape; weight and slot ids."""
+    return N * L * (3 * H * e + H * e + H * K * e) + N * H * K * e + H * K * e + 4 * N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("bwd.hip", "common.hpp", "kernels.hpp"):
+        with open(os.path.join(ROOT, "gated_short_causal_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(per_launch_algo_bytes):
+    """HBM bytes of one backward launch from the committed counter summary, if it matches the current source."""
+    path = os.path.join(ROOT, "profiles", "backward_T65536_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_backward_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl_mod, T, H, K, n_channels):
+    """The fp64 oracle (as it stands) on the same workload restricted to n_channels channels
+    (channels are independent, so this is the same arithmetic on a slice)."""
+    import torch
+    import oracle
+    c = wl_mod.train_lfm2(T=T)
+    chans = torch.arange(n_channels)
+    cols = torch.cat([chans, chans + H, chans + 2 * H])
+    inp = oracle.f64(c.inp[:, cols])
+    w = oracle.f64(c.w[chans])
+    dy = oracle.f64(c.dy[:, chans])
+    threads = min(16, len(os.sched_getaffinity(0)))
+    oracle.set_threads(threads)
+    t0 = time.perf_counter()
+    oracle.prefill(inp, c.cu, w)
+    oracle.backward(inp, c.cu, w, dy)
+    dt = time.perf_counter() - t0
+    nbytes = algo_bytes_fwd(T, n_channels, K, 2) + algo_bytes_bwd(T, n_channels, K, 2)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fwd+bwd, T={T}, first {n_channels} of {H} channels, K={K}, bf16 inputs widened to fp64; "
+                      f"{dt:.2f} s wall", "seconds": round(dt, 3)}
+
+
+def timed_loop(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def extra_measurements(wl_mod, g, steps):
+    """Decode, ragged prefill and verify at their LFM2-1.2B shapes, rotating input sets past the 256 MB
+    Infinity Cache so the numbers are HBM numbers (host launch overhead included for the tiny calls)."""
+    import torch
+    from gated_short_causal_amd import lfm2sc_decode_step, lfm2sc_prefill_ragged, lfm2sc_verify_window
+    dev = torch.device("cuda")
+    out = {}
+    # decode: 10.5 MB per call, 64 rotated sets
+    sets = [wl_mod.decode_lfm2(seed=200 + i).to(dev) for i in range(64)]
+    ys = [torch.empty(256, 2048, dtype=torch.bfloat16, device=dev) for _ in sets]
+    i = [0]
+
+    def dec():
+        s = sets[i[0] % 64]
+        lfm2sc_decode_step(s.inp, s.w, s.pool, s.slot_idx, ys[i[0] % 64])
+        i[0] += 1
+    ms = timed_loop(dec, steps * 64, 64)
+    b = algo_bytes_decode(256, 2048, 3, 2)
+    out["decode_N256"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
+    del sets, ys
+    # ragged prefill: ~138 MB per call, 5 rotated sets
+    sets = [wl_mod.ragged_prefill_lfm2(seed=300 + i).to(dev) for i in range(5)]
+    ys = [torch.empty(s.inp.shape[0], 2048, dtype=torch.bfloat16, device=dev) for s in sets]
+    j = [0]
+
+    def pre():
+        s = sets[j[0] % 5]
+        lfm2sc_prefill_ragged(s.inp, s.cu, s.w, ys[j[0] % 5], s.pool, s.slot_idx)
+        j[0] += 1
+    ms = timed_loop(pre, steps * 5, 5)
+    b = sum(algo_bytes_prefill(s.inp.shape[0], 8, 2048, 3, 2) for s in sets) / len(sets)
+    out["ragged_prefill_N8"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": int(b)}
+    del sets, ys
+    # verify: 15.5 MB per call, 48 rotated sets
+    sets = [wl_mod.verify_lfm2(seed=400 + i).to(dev) for i in range(48)]
+    outs = [(torch.empty(512, 2048, dtype=torch.bfloat16, device=dev),
+             torch.empty(64, 8, 2048, 3, dtype=torch.bfloat16, device=dev)) for _ in sets]
+    k = [0]
+
+    def ver():
+        s = sets[k[0] % 48]
+        y, win = outs[k[0] % 48]
+        lfm2sc_verify_window(s.inp, s.w, s.pool, s.slot_idx, 8, win, y)
+        k[0] += 1
+    ms = timed_loop(ver, steps * 48, 48)
+    b = algo_bytes_verify(64, 8, 2048, 3, 2)
+    out["verify_64x8"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
+    return out
+
+
+def calibrate_copy():
+    """A plain device-to-device copy of 1 GiB, 5 times: the FETCH_SIZE / WRITE_SIZE readings of this kernel
+    under rocprofv3 give the counter-to-bytes factor (1 GiB read and 1 GiB written per dispatch)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--T", type=int, default=65536)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-channels", type=int, default=2048)
+    ap.add_argument("--extra", action="store_true", help="also time decode, ragged prefill and verify")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the ShortConv path is sharded by channels or "
+              "sequences with no collective on the hot path, and no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    from gated_short_causal_amd import lfm2sc_backward, lfm2sc_backward_workspace_bytes, lfm2sc_prefill_ragged
+    from gated_short_causal_amd import workloads as wl
+
+    T, H, K, e = args.T, 2048, 3, 2
+    dev = torch.device("cuda")
+    print(f"bench: generating T={T} inputs", file=sys.stderr, flush=True)
+    c = wl.train_lfm2(T=T).to(dev)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    d_in = torch.empty(T, 3 * H, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(H, K, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, lfm2sc_backward_workspace_bytes(torch.bfloat16, H, K, T, 1)), dtype=torch.uint8,
+                     device=dev)
+
+    def fwd():
+        lfm2sc_prefill_ragged(c.inp, c.cu, c.w, y)
+
+    def bwd():
+        lfm2sc_backward(c.inp, c.cu, c.w, c.dy, d_in, dW, ws)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        ev[s][0].record()
+        fwd()
+        ev[s][1].record()
+        bwd()
+        ev[s][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    bwd_ms = sum(b.elapsed_time(cc) for _, b, cc in ev) / args.steps
+    step_bytes = algo_bytes_fwd(T, H, K, e) + algo_bytes_bwd(T, H, K, e)
+    bwd_bytes = algo_bytes_bwd(T, H, K, e)
+    value = step_bytes / ms_step / 1e6
+    bwd_gbs = bwd_bytes / bwd_ms / 1e6
+    traffic = read_traffic(bwd_bytes)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs and dy, U(-0.5,0.5) weight)",
+        "config": {"workload": f"ShortConv training step (prefill forward + backward), 1 sequence, T={T}, "
+                               f"H={H}, K={K}, bf16 I/O, fp32 accumulation, zero initial state",
+                   "T": T, "H": H, "K": K, "seqs": 1},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(bwd_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bwd_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "lfm2sc_backward (backward_kernel + dw_finish_kernel, one call)",
+                     "algorithmic_bytes_per_launch": bwd_bytes},
+        "context": {"pages_mi325x_liger_fwd_bwd_ms": {"T=4096": 0.463, "T=65536": 8.083}},
+    }
+    if args.extra:
+        line["extra"] = extra_measurements(wl, None, max(1, args.steps // 4))
+    if not args.no_cpu:
+        print("bench: timing the oracle CPU baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(wl, T, H, K, args.cpu_channels)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

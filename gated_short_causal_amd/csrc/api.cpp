@@ -132,7 +132,7 @@ int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t 
     a.pool = static_cast<const E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
     a.dy = static_cast<const E*>(dy); a.dy_stride = dy_stride;
     a.din = static_cast<E*>(din); a.din_stride = din_stride;
-    a.partial = static_cast<float*>(ws);
+    a.partial = ws;
     a.dW = dW;
     a.H = H;
     a.sub = backward_sub(total_T, H);
@@ -140,10 +140,10 @@ int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t 
     return launched("lfm2sc_backward", launch_backward<E>(a, K, s));
 }
 
-size_t workspace_bytes(int H, int K, int64_t total_T, int N) {
+size_t workspace_bytes(int dtype, int H, int K, int64_t total_T, int N) {
     if (N <= 0 || total_T <= 0) return 0;
     const int64_t nt = ragged_tiles(total_T, N, backward_sub(total_T, H));
-    const size_t bytes = (size_t)nt * (size_t)H * (size_t)K * sizeof(float);
+    const size_t bytes = (size_t)nt * (size_t)H * (size_t)K * (size_t)backward_partial_bytes(dtype == LFM2SC_F32);
     return (bytes + 255) / 256 * 256;
 }
 
@@ -283,7 +283,7 @@ size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T,
     if (dtype != LFM2SC_BF16 && dtype != LFM2SC_F32) return 0;
     if (H < 8 || H % 8 != 0 || H > kMaxH || K < 1 || K > 4) return 0;
     if (total_T < 0 || total_T >= kMaxRows || num_seqs < 0) return 0;
-    return workspace_bytes(H, K, total_T, num_seqs);
+    return workspace_bytes(dtype, H, K, total_T, num_seqs);
 }
 
 int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T,
@@ -311,7 +311,7 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
             TRY(check_pool(fn, init_state_pool, num_slots, slot_stride, slot_idx, H, K));
         if (ragged_tiles(total_T, num_seqs, backward_sub(total_T, H)) >= (1 << 30))
             return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many sequences/tokens for one launch", fn);
-        const size_t need = workspace_bytes(H, K, total_T, num_seqs);
+        const size_t need = workspace_bytes(dtype, H, K, total_T, num_seqs);
         if (workspace == nullptr || workspace_bytes_ < need)
             return fail(LFM2SC_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace,
                         workspace_bytes_, need);

@@ -27,34 +27,49 @@
 
 namespace lfm2sc {
 
+// Internal arithmetic type of the backward: fp32 for bf16 I/O (products of
+// two bf16 values are exact in fp32), fp64 for fp32 I/O (products of two fp32
+// values are exact in fp64).  dW is a reduction over every token of a
+// sequence, so this keeps its only rounding at the final fp32 store even when
+// thousands of terms cancel.
+template <typename E> struct BwdAcc { using type = float; };
+template <> struct BwdAcc<float> { using type = double; };
+
 template <typename E, int K>
 struct BwdState {
+    using A = typename BwdAcc<E>::type;
     static constexpr int KH = K > 1 ? K - 1 : 1;
-    float wf[kChPerLane][K];
-    float hist[kChPerLane][KH];   // X[r+1 .. r+K-1] for the current row r
-    float gw[kChPerLane][K];      // gw[c][a] = g[r-a]
+    A wf[kChPerLane][K];
+    A hist[kChPerLane][KH];       // X[r+1 .. r+K-1] for the current row r
+    A gw[kChPerLane][K];          // gw[c][a] = g[r-a]
     Raw8<E> fb[KH], fx[KH];       // fb[a] = B of row r-1-a (same for xv)
-    float acc[kChPerLane][K];     // dW partial
+    A acc[kChPerLane][K];         // dW partial
 };
+
+template <typename A>
+__device__ __forceinline__ A fma_a(A a, A b, A c) { return a * b + c; }
+template <> __device__ __forceinline__ float fma_a<float>(float a, float b, float c) { return fmaf(a, b, c); }
+template <> __device__ __forceinline__ double fma_a<double>(double a, double b, double c) { return fma(a, b, c); }
 
 // Row r of the window: all four operands loaded.  Emits dC[r] and, if `emit`,
 // dB/dxv of u = r-K+1.
 template <typename E, int K>
 __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, const Raw8<E>& rb, const Raw8<E>& rc,
                                         const Raw8<E>& rx, E* dc_p, bool emit, E* db_p, E* dxv_p) {
+    using A = typename BwdState<E, K>::A;
     float dy[8], b[8], c[8], x[8], dC[8];
     to_f32(rdy, dy); to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
-        const float g = dy[ch] * c[ch];
-        const float bx = b[ch] * x[ch];
-        float conv = st.wf[ch][K - 1] * bx;
+        const A g = (A)dy[ch] * (A)c[ch];
+        const A bx = (A)b[ch] * (A)x[ch];
+        A conv = st.wf[ch][K - 1] * bx;
 #pragma unroll
-        for (int k = 0; k < K - 1; ++k) conv = fmaf(st.wf[ch][k], st.hist[ch][k], conv);
-        dC[ch] = dy[ch] * conv;
+        for (int k = 0; k < K - 1; ++k) conv = fma_a<A>(st.wf[ch][k], st.hist[ch][k], conv);
+        dC[ch] = (float)((A)dy[ch] * conv);
 #pragma unroll
-        for (int k = 0; k < K - 1; ++k) st.acc[ch][k] = fmaf(g, st.hist[ch][k], st.acc[ch][k]);
-        st.acc[ch][K - 1] = fmaf(g, bx, st.acc[ch][K - 1]);
+        for (int k = 0; k < K - 1; ++k) st.acc[ch][k] = fma_a<A>(g, st.hist[ch][k], st.acc[ch][k]);
+        st.acc[ch][K - 1] = fma_a<A>(g, bx, st.acc[ch][K - 1]);
         if constexpr (K > 1) {
 #pragma unroll
             for (int k = 0; k < K - 2; ++k) st.hist[ch][k] = st.hist[ch][k + 1];
@@ -72,11 +87,11 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
         float dB[8], dX[8];
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
-            float dbx = st.wf[ch][0] * st.gw[ch][0];
+            A dbx = st.wf[ch][0] * st.gw[ch][0];
 #pragma unroll
-            for (int k = 1; k < K; ++k) dbx = fmaf(st.wf[ch][k], st.gw[ch][k], dbx);
-            dB[ch] = dbx * xu[ch];
-            dX[ch] = dbx * bu[ch];
+            for (int k = 1; k < K; ++k) dbx = fma_a<A>(st.wf[ch][k], st.gw[ch][k], dbx);
+            dB[ch] = (float)(dbx * (A)xu[ch]);
+            dX[ch] = (float)(dbx * (A)bu[ch]);
         }
         store_f32x8<E>(db_p, dB);
         store_f32x8<E>(dxv_p, dX);
@@ -91,7 +106,9 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
 // Row r at or past the window end: only g[r] is needed (0 past the sequence
 // end); emits dB/dxv of u = r-K+1 when u is inside the window.
 template <typename E, int K>
-__device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const float* g, bool emit, E* db_p, E* dxv_p) {
+__device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const typename BwdState<E, K>::A* g, bool emit,
+                                             E* db_p, E* dxv_p) {
+    using A = typename BwdState<E, K>::A;
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
 #pragma unroll
@@ -105,11 +122,11 @@ __device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const float* g,
         float dB[8], dX[8];
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
-            float dbx = st.wf[ch][0] * st.gw[ch][0];
+            A dbx = st.wf[ch][0] * st.gw[ch][0];
 #pragma unroll
-            for (int k = 1; k < K; ++k) dbx = fmaf(st.wf[ch][k], st.gw[ch][k], dbx);
-            dB[ch] = dbx * xu[ch];
-            dX[ch] = dbx * bu[ch];
+            for (int k = 1; k < K; ++k) dbx = fma_a<A>(st.wf[ch][k], st.gw[ch][k], dbx);
+            dB[ch] = (float)(dbx * (A)xu[ch]);
+            dX[ch] = (float)(dbx * (A)bu[ch]);
         }
         store_f32x8<E>(db_p, dB);
         store_f32x8<E>(dxv_p, dX);
@@ -130,6 +147,7 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
 
     // History X[lo+1 .. lo+K-1]: initial-state entries (index < K) or bx of
     // earlier rows of this sequence.
+    using A = typename BwdState<E, K>::A;
     if constexpr (K > 1) {
         float s0[kChPerLane][K];
         bool have_s0 = false;
@@ -145,14 +163,14 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
             const int64_t j = lo + 1 + k;
             if (j < K) {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) st.hist[c][k] = have_s0 ? s0[c][j] : 0.f;
+                for (int c = 0; c < 8; ++c) st.hist[c][k] = have_s0 ? (A)s0[c][j] : (A)0;
             } else {
                 const E* row = ib + (r0 + j - K) * a.in_stride;
                 float b[8], x[8];
                 load_f32x8<E>(row, b);
                 load_f32x8<E>(row + 2 * H, x);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) st.hist[c][k] = b[c] * x[c];
+                for (int c = 0; c < 8; ++c) st.hist[c][k] = (A)b[c] * (A)x[c];
             }
         }
     }
@@ -193,16 +211,16 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
     // K-1 rows past the window: g only, from the next rows of the sequence.
     if constexpr (K > 1) {
         for (; r < hi + K - 1; ++r) {
-            float g[8];
+            A g[8];
             if (r < T) {
                 float dyv[8], cv[8];
                 load_f32x8<E>(gb + (r0 + r) * a.dy_stride, dyv);
                 load_f32x8<E>(ib + (r0 + r) * a.in_stride + H, cv);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) g[c] = dyv[c] * cv[c];
+                for (int c = 0; c < 8; ++c) g[c] = (A)dyv[c] * (A)cv[c];
             } else {
 #pragma unroll
-                for (int c = 0; c < 8; ++c) g[c] = 0.f;
+                for (int c = 0; c < 8; ++c) g[c] = (A)0;
             }
             const int64_t u = r - (K - 1);
             E* up = db + (r0 + u) * a.din_stride;
@@ -213,6 +231,7 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
 
 template <typename E, int K, int U>
 __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E> a) {
+    using A = typename BwdState<E, K>::A;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -223,76 +242,86 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int k = 0; k < K; ++k) { st.acc[c][k] = 0.f; st.gw[c][k] = 0.f; }
+        for (int k = 0; k < K; ++k) { st.acc[c][k] = (A)0; st.gw[c][k] = (A)0; }
 
     if (lane_on) {
         const int64_t gap = (int64_t)a.sub * kWavesPerBlock;
         const int64_t v0 = (int64_t)tile * gap + (int64_t)wave * a.sub;
         SeqSpan sp;
         if (find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) {
-            load_block<E, K>(a.w + (int64_t)ch0 * K, st.wf);
+            float wf[kChPerLane][K];
+            load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int k = 0; k < K; ++k) st.wf[c][k] = (A)wf[c][k];
             bwd_window<E, K, U>(a, sp, ch0, st);
         }
     }
 
-    // Sum the 4 waves' dW partials (same channels, consecutive windows).
-    __shared__ float red[kWavesPerBlock][kChPerLane * K][kWave];
+    // Sum the 4 waves' dW partials (same channels, consecutive windows) in a
+    // fixed order and write one partial row [H*K] per workgroup window.
+    __shared__ A red[kWavesPerBlock][kChPerLane * K][kWave];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int k = 0; k < K; ++k) red[wave][c * K + k][lane] = st.acc[c][k];
     __syncthreads();
     if (wave == 0 && lane_on) {
-        float out[kChPerLane * K];
+        A* dst = static_cast<A*>(a.partial) + (int64_t)tile * a.H * K + (int64_t)ch0 * K;
 #pragma unroll
         for (int e = 0; e < kChPerLane * K; ++e)
-            out[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
-        float4* dst = reinterpret_cast<float4*>(a.partial + (int64_t)tile * a.H * K + (int64_t)ch0 * K);
-#pragma unroll
-        for (int q = 0; q < 2 * K; ++q) dst[q] = make_float4(out[4 * q], out[4 * q + 1], out[4 * q + 2], out[4 * q + 3]);
+            dst[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
     }
 }
 
 // dW[j] = sum over windows of partial[window][j], j in [0, H*K): 32 columns x
-// 32 row groups per workgroup, then a fixed-order sum of the 32 row groups.
+// 32 row groups per workgroup, then a fixed-order sum of the 32 row groups;
+// one rounding to fp32 at the store.
 constexpr int kFinCols = 32;
 constexpr int kFinRows = 32;
 
-__global__ __launch_bounds__(kFinCols * kFinRows) void dw_finish_kernel(const float* __restrict__ partial,
-                                                                       int64_t ntiles, int64_t HK, float* __restrict__ dW) {
+template <typename A>
+__global__ __launch_bounds__(kFinCols * kFinRows) void dw_finish_kernel(const A* __restrict__ partial, int64_t ntiles,
+                                                                       int64_t HK, float* __restrict__ dW) {
     const int col = threadIdx.x % kFinCols;
     const int rg = threadIdx.x / kFinCols;
     const int64_t j = (int64_t)blockIdx.x * kFinCols + col;
-    float s = 0.f;
+    A s = (A)0;
     if (j < HK) {
 #pragma unroll 8
         for (int64_t r = rg; r < ntiles; r += kFinRows) s += partial[r * HK + j];
     }
-    __shared__ float red[kFinRows][kFinCols + 1];
+    __shared__ A red[kFinRows][kFinCols + 1];
     red[rg][col] = s;
     __syncthreads();
     if (rg == 0 && j < HK) {
-        float t = 0.f;
+        A t = (A)0;
 #pragma unroll
         for (int q = 0; q < kFinRows; ++q) t += red[q][col];
-        dW[j] = t;
+        dW[j] = (float)t;
     }
 }
 
 template <typename E, int K>
 static hipError_t backward_k(const BackwardArgs<E>& a, hipStream_t s) {
+    using A = typename BwdAcc<E>::type;
     if (a.ntiles > 0) {
         const int gy = (a.H + kChPerWave - 1) / kChPerWave;
         const int gx = pad_xcd(a.ntiles);
-        hipLaunchKernelGGL((backward_kernel<E, K, 4>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+        // fp32 I/O carries fp64 state: fewer rows in flight keep it in registers
+        constexpr int U = sizeof(A) == 8 ? 2 : 4;
+        hipLaunchKernelGGL((backward_kernel<E, K, U>), dim3(gx, gy), dim3(kThreads), 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t HK = (int64_t)a.H * K;
-    hipLaunchKernelGGL(dw_finish_kernel, dim3((unsigned)((HK + kFinCols - 1) / kFinCols)), dim3(kFinCols * kFinRows), 0, s,
-                       (const float*)a.partial, (int64_t)a.ntiles, HK, a.dW);
+    hipLaunchKernelGGL((dw_finish_kernel<A>), dim3((unsigned)((HK + kFinCols - 1) / kFinCols)),
+                       dim3(kFinCols * kFinRows), 0, s, (const A*)a.partial, (int64_t)a.ntiles, HK, a.dW);
     return hipGetLastError();
 }
+
+int backward_partial_bytes(int dtype_is_f32) { return dtype_is_f32 ? (int)sizeof(double) : (int)sizeof(float); }
 
 template <typename E>
 hipError_t launch_backward(const BackwardArgs<E>& a, int K, hipStream_t s) {

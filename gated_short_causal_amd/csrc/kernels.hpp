@@ -54,7 +54,7 @@ struct BackwardArgs {
     const E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     const E* dy; int64_t dy_stride;
     E* din; int64_t din_stride;
-    float* partial;   // [ntiles][H*K] fp32 per-window dW sums
+    void* partial;    // [ntiles][H*K] per-window dW sums (fp32 for bf16 I/O, fp64 for fp32 I/O)
     float* dW;        // [H][K]
     int H;
     int sub;
@@ -65,6 +65,7 @@ struct BackwardArgs {
 int prefill_sub(int64_t total_T, int H);
 int backward_sub(int64_t total_T, int H);
 int64_t ragged_tiles(int64_t total_T, int N, int sub);
+int backward_partial_bytes(int dtype_is_f32);   // bytes per dW partial element
 
 template <typename E> hipError_t launch_prefill(const PrefillArgs<E>& a, int K, hipStream_t s);
 template <typename E> hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s);
