@@ -10,7 +10,8 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime before the library)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "liblfm2sc.so")
+# LFM2SC_LIB may name another build of the same library (e.g. a tuning variant) to load instead.
+LIB_PATH = os.environ.get("LFM2SC_LIB") or os.path.join(_PKG, "liblfm2sc.so")
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64

@@ -115,8 +115,8 @@ int prefill_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t t
     a.pool = static_cast<E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
     a.y = static_cast<E*>(y); a.y_stride = y_stride;
     a.H = H;
-    a.sub = prefill_sub(total_T, H);
-    a.ntiles = (int)ragged_tiles(total_T, N, a.sub);
+    a.sub = 0;
+    a.ntiles = 0;
     return launched("lfm2sc_prefill_ragged", launch_prefill<E>(a, K, s));
 }
 
@@ -135,14 +135,14 @@ int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t 
     a.partial = ws;
     a.dW = dW;
     a.H = H;
-    a.sub = backward_sub(total_T, H);
-    a.ntiles = (N > 0 && total_T > 0) ? (int)ragged_tiles(total_T, N, a.sub) : 0;
+    a.sub = 0;
+    a.ntiles = 0;
     return launched("lfm2sc_backward", launch_backward<E>(a, K, s));
 }
 
 size_t workspace_bytes(int dtype, int H, int K, int64_t total_T, int N) {
     if (N <= 0 || total_T <= 0) return 0;
-    const int64_t nt = ragged_tiles(total_T, N, backward_sub(total_T, H));
+    const int64_t nt = backward_partial_rows(dtype == LFM2SC_F32, H, K, total_T, N);
     const size_t bytes = (size_t)nt * (size_t)H * (size_t)K * (size_t)backward_partial_bytes(dtype == LFM2SC_F32);
     return (bytes + 255) / 256 * 256;
 }
@@ -186,7 +186,7 @@ int lfm2sc_prefill_ragged(int dtype, int H, int K, const void* in_proj, int64_t 
     TRY(check_ptr(fn, "weight", weight, 16));
     TRY(check_ptr(fn, "y", y, 16));
     if (state_pool != nullptr) TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
-    if (ragged_tiles(total_T, num_seqs, prefill_sub(total_T, H)) >= (1 << 30))
+    if (ragged_tiles_bound(total_T, num_seqs) >= (1 << 30))
         return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many sequences/tokens for one launch", fn);
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, state_pool ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens, total_T, nullptr, 0));
@@ -309,7 +309,7 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
         TRY(check_ptr(fn, "d_in_proj", d_in_proj, 16));
         if (init_state_pool != nullptr)
             TRY(check_pool(fn, init_state_pool, num_slots, slot_stride, slot_idx, H, K));
-        if (ragged_tiles(total_T, num_seqs, backward_sub(total_T, H)) >= (1 << 30))
+        if (ragged_tiles_bound(total_T, num_seqs) >= (1 << 30))
             return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many sequences/tokens for one launch", fn);
         const size_t need = workspace_bytes(dtype, H, K, total_T, num_seqs);
         if (workspace == nullptr || workspace_bytes_ < need)

@@ -53,9 +53,13 @@ template <> __device__ __forceinline__ double fma_a<double>(double a, double b, 
 
 // Row r of the window: all four operands loaded.  Emits dC[r] and, if `emit`,
 // dB/dxv of u = r-K+1.
+// Per-lane byte offsets of the lane's 8 channels in a d_in row (dB | dC | dxv).
+struct DinOffsets { uint32_t b, c, x; };
+
 template <typename E, int K>
 __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, const Raw8<E>& rb, const Raw8<E>& rc,
-                                        const Raw8<E>& rx, E* dc_p, bool emit, E* db_p, E* dxv_p) {
+                                        const Raw8<E>& rx, rsrc_t dc_row, bool emit, rsrc_t du_row,
+                                        const DinOffsets& o) {
     using A = typename BwdState<E, K>::A;
     float dy[8], b[8], c[8], x[8], dC[8];
     to_f32(rdy, dy); to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
@@ -79,7 +83,7 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
         for (int a = K - 1; a > 0; --a) st.gw[ch][a] = st.gw[ch][a - 1];
         st.gw[ch][0] = g;
     }
-    store_f32x8<E>(dc_p, dC);
+    bst8f<E, LFM2SC_BWD_NT>(dc_row, o.c, dC);
     if (emit) {
         float bu[8], xu[8];
         if constexpr (K > 1) { to_f32(st.fb[K - 2], bu); to_f32(st.fx[K - 2], xu); }
@@ -93,8 +97,8 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
             dB[ch] = (float)(dbx * (A)xu[ch]);
             dX[ch] = (float)(dbx * (A)bu[ch]);
         }
-        store_f32x8<E>(db_p, dB);
-        store_f32x8<E>(dxv_p, dX);
+        bst8f<E, LFM2SC_BWD_NT>(du_row, o.b, dB);
+        bst8f<E, LFM2SC_BWD_NT>(du_row, o.x, dX);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -107,7 +111,7 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
 // end); emits dB/dxv of u = r-K+1 when u is inside the window.
 template <typename E, int K>
 __device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const typename BwdState<E, K>::A* g, bool emit,
-                                             E* db_p, E* dxv_p) {
+                                             rsrc_t du_row, const DinOffsets& o) {
     using A = typename BwdState<E, K>::A;
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
@@ -128,8 +132,8 @@ __device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const typename 
             dB[ch] = (float)(dbx * (A)xu[ch]);
             dX[ch] = (float)(dbx * (A)bu[ch]);
         }
-        store_f32x8<E>(db_p, dB);
-        store_f32x8<E>(dxv_p, dX);
+        bst8f<E, LFM2SC_BWD_NT>(du_row, o.b, dB);
+        bst8f<E, LFM2SC_BWD_NT>(du_row, o.x, dX);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -142,8 +146,6 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
     const int H = a.H;
     const int64_t lo = sp.lo, hi = sp.hi, T = sp.T, r0 = sp.r0;
     const E* ib = a.in + ch0;
-    const E* gb = a.dy + ch0;
-    E* db = a.din + ch0;
 
     // History X[lo+1 .. lo+K-1]: initial-state entries (index < K) or bx of
     // earlier rows of this sequence.
@@ -175,38 +177,95 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
         }
     }
 
+    // Streamed rows go through buffer descriptors (see row_rsrc).
+    const uint32_t eb = sizeof(E);
+    const DinOffsets o{(uint32_t)ch0 * eb, (uint32_t)(ch0 + H) * eb, (uint32_t)(ch0 + 2 * H) * eb};
+    const uint32_t in_bytes = 3u * (uint32_t)H * eb, dy_bytes = (uint32_t)H * eb;
+    const E* in_rows = a.in + r0 * a.in_stride;
+    const E* dy_rows = a.dy + r0 * a.dy_stride;
+    E* din_rows = a.din + r0 * a.din_stride;
+    auto in_row = [&](int64_t t) { return row_rsrc(in_rows + t * a.in_stride, in_bytes); };
+    auto dy_row = [&](int64_t t) { return row_rsrc(dy_rows + t * a.dy_stride, dy_bytes); };
+    auto din_row = [&](int64_t t) { return row_rsrc(din_rows + t * a.din_stride, in_bytes); };
+    auto load_batch = [&](Raw8<E> (&rdy)[U], Raw8<E> (&rb)[U], Raw8<E> (&rc)[U], Raw8<E> (&rx)[U], int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const rsrc_t ir = in_row(t0 + u);
+            rdy[u] = bld8<E, LFM2SC_BWD_NT>(dy_row(t0 + u), o.b);
+            rb[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.b);
+            rc[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.c);
+            rx[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.x);
+        }
+    };
+    auto use_batch = [&](const Raw8<E> (&rdy)[U], const Raw8<E> (&rb)[U], const Raw8<E> (&rc)[U],
+                         const Raw8<E> (&rx)[U], int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], din_row(t0 + u), true, din_row(t0 + u - (K - 1)), o);
+    };
+
     // Rows whose u = r-K+1 is still before the window: no dB/dxv emitted.
     int64_t r = lo;
     const int64_t head_end = (lo + K - 1 < hi) ? lo + K - 1 : hi;
     for (; r < head_end; ++r) {
-        const E* row = ib + (r0 + r) * a.in_stride;
-        bwd_row<E, K>(st, ld8<E>(gb + (r0 + r) * a.dy_stride), ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H),
-                      db + (r0 + r) * a.din_stride + H, false, nullptr, nullptr);
+        const rsrc_t ir = in_row(r);
+        bwd_row<E, K>(st, bld8<E, LFM2SC_BWD_NT>(dy_row(r), o.b), bld8<E, LFM2SC_BWD_NT>(ir, o.b),
+                      bld8<E, LFM2SC_BWD_NT>(ir, o.c), bld8<E, LFM2SC_BWD_NT>(ir, o.x), din_row(r), false, din_row(r),
+                      o);
     }
-    // Steady state: U rows of loads in flight, then U rows of arithmetic.
+    // Steady state: batches of U rows of loads in flight (two register stages
+    // with LFM2SC_BWD_PIPE, so the next batch is issued before this one is used).
+#if LFM2SC_BWD_PIPE
+    if (r + U <= hi) {
+        Raw8<E> ady[U], ab[U], ac[U], ax[U], bdy[U], bb[U], bc[U], bxr[U];
+        load_batch(ady, ab, ac, ax, r);
+        while (true) {
+            if (r + 2 * U <= hi) {
+                load_batch(bdy, bb, bc, bxr, r + U);
+                use_batch(ady, ab, ac, ax, r);
+                r += U;
+            } else {
+                use_batch(ady, ab, ac, ax, r);
+                r += U;
+                break;
+            }
+            if (r + 2 * U <= hi) {
+                load_batch(ady, ab, ac, ax, r + U);
+                use_batch(bdy, bb, bc, bxr, r);
+                r += U;
+            } else {
+                use_batch(bdy, bb, bc, bxr, r);
+                r += U;
+                break;
+            }
+        }
+    }
+#else
     for (; r + U <= hi; r += U) {
+        Raw8<E> rdy[U], rb[U], rc[U], rx[U];
+        load_batch(rdy, rb, rc, rx, r);
+        use_batch(rdy, rb, rc, rx, r);
+    }
+#endif
+    // Remainder (< U rows): one partial batch, all its loads issued together.
+    if (r < hi) {
+        const int n = (int)(hi - r);
         Raw8<E> rdy[U], rb[U], rc[U], rx[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const E* row = ib + (r0 + r + u) * a.in_stride;
-            rdy[u] = ld8<E>(gb + (r0 + r + u) * a.dy_stride);
-            rb[u] = ld8<E>(row);
-            rc[u] = ld8<E>(row + H);
-            rx[u] = ld8<E>(row + 2 * H);
+            if (u < n) {
+                const rsrc_t ir = in_row(r + u);
+                rdy[u] = bld8<E, LFM2SC_BWD_NT>(dy_row(r + u), o.b);
+                rb[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.b);
+                rc[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.c);
+                rx[u] = bld8<E, LFM2SC_BWD_NT>(ir, o.x);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t rr = r0 + r + u;
-            E* up = db + (rr - (K - 1)) * a.din_stride;
-            bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], db + rr * a.din_stride + H, true, up, up + 2 * H);
-        }
-    }
-    for (; r < hi; ++r) {
-        const int64_t rr = r0 + r;
-        const E* row = ib + rr * a.in_stride;
-        E* up = db + (rr - (K - 1)) * a.din_stride;
-        bwd_row<E, K>(st, ld8<E>(gb + rr * a.dy_stride), ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H),
-                      db + rr * a.din_stride + H, true, up, up + 2 * H);
+        for (int u = 0; u < U; ++u)
+            if (u < n)
+                bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], din_row(r + u), true, din_row(r + u - (K - 1)), o);
+        r = hi;
     }
     // K-1 rows past the window: g only, from the next rows of the sequence.
     if constexpr (K > 1) {
@@ -214,8 +273,8 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
             A g[8];
             if (r < T) {
                 float dyv[8], cv[8];
-                load_f32x8<E>(gb + (r0 + r) * a.dy_stride, dyv);
-                load_f32x8<E>(ib + (r0 + r) * a.in_stride + H, cv);
+                to_f32(bld8<E, 0>(dy_row(r), o.b), dyv);
+                to_f32(bld8<E, 0>(in_row(r), o.c), cv);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) g[c] = (A)dyv[c] * (A)cv[c];
             } else {
@@ -223,8 +282,7 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
                 for (int c = 0; c < 8; ++c) g[c] = (A)0;
             }
             const int64_t u = r - (K - 1);
-            E* up = db + (r0 + u) * a.din_stride;
-            bwd_tail_row<E, K>(st, g, u >= lo, up, up + 2 * H);
+            bwd_tail_row<E, K>(st, g, u >= lo, din_row(u), o);
         }
     }
 }
@@ -232,10 +290,12 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
 template <typename E, int K, int U>
 __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E> a) {
     using A = typename BwdState<E, K>::A;
+    constexpr int TW = LFM2SC_BWD_TW;
+    using Lay = WgLayout<TW>;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int ch0 = (blockIdx.y * kWave + lane) * kChPerLane;
+    const int ch0 = ((blockIdx.y * Lay::kCW + wave / TW) * kWave + lane) * kChPerLane;
     const bool lane_on = tile < a.ntiles && ch0 < a.H;
 
     BwdState<E, K> st;
@@ -245,8 +305,8 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
         for (int k = 0; k < K; ++k) { st.acc[c][k] = (A)0; st.gw[c][k] = (A)0; }
 
     if (lane_on) {
-        const int64_t gap = (int64_t)a.sub * kWavesPerBlock;
-        const int64_t v0 = (int64_t)tile * gap + (int64_t)wave * a.sub;
+        const int64_t gap = (int64_t)a.sub * TW;
+        const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % TW) * a.sub;
         SeqSpan sp;
         if (find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) {
             float wf[kChPerLane][K];
@@ -259,19 +319,33 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
         }
     }
 
-    // Sum the 4 waves' dW partials (same channels, consecutive windows) in a
-    // fixed order and write one partial row [H*K] per workgroup window.
-    __shared__ A red[kWavesPerBlock][kChPerLane * K][kWave];
+    // dW partial of this workgroup window: the TW waves that share channels
+    // (consecutive windows) are summed through LDS in a fixed order; one
+    // partial row [H*K] per workgroup window goes to the workspace.
+    A* dst = static_cast<A*>(a.partial) + (int64_t)tile * a.H * K + (int64_t)ch0 * K;
+    if constexpr (TW == 1) {
+        if (lane_on) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+            for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int k = 0; k < K; ++k) red[wave][c * K + k][lane] = st.acc[c][k];
-    __syncthreads();
-    if (wave == 0 && lane_on) {
-        A* dst = static_cast<A*>(a.partial) + (int64_t)tile * a.H * K + (int64_t)ch0 * K;
+                for (int k = 0; k < K; ++k) dst[c * K + k] = st.acc[c][k];
+        }
+    } else {
+        __shared__ A red[kWavesPerBlock][kChPerLane * K][kWave];
 #pragma unroll
-        for (int e = 0; e < kChPerLane * K; ++e)
-            dst[e] = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int k = 0; k < K; ++k) red[wave][c * K + k][lane] = st.acc[c][k];
+        __syncthreads();
+        if (wave % TW == 0 && lane_on) {
+#pragma unroll
+            for (int e = 0; e < kChPerLane * K; ++e) {
+                A v = red[wave][e][lane];
+#pragma unroll
+                for (int q = 1; q < TW; ++q) v += red[wave + q][e][lane];
+                dst[e] = v;
+            }
+        }
     }
 }
 
@@ -303,22 +377,51 @@ __global__ __launch_bounds__(kFinCols * kFinRows) void dw_finish_kernel(const A*
     }
 }
 
+// fp32 I/O carries fp64 state: fewer rows in flight keep it in registers.
+template <typename E> constexpr int bwd_unroll() { return sizeof(typename BwdAcc<E>::type) == 8 ? 2 : LFM2SC_BWD_U; }
+
 template <typename E, int K>
-static hipError_t backward_k(const BackwardArgs<E>& a, hipStream_t s) {
+static Tiling backward_tiling(int64_t total_T, int N, int H) {
+    constexpr auto kernel = backward_kernel<E, K, bwd_unroll<E>()>;
+    static const int resident = resident_workgroups(kernel, LFM2SC_BWD_LDS);
+    return ragged_tiling(total_T, N, WgLayout<LFM2SC_BWD_TW>::groups(H), resident, LFM2SC_BWD_TW);
+}
+
+template <typename E, int K>
+static hipError_t backward_k(BackwardArgs<E> a, hipStream_t s) {
     using A = typename BwdAcc<E>::type;
-    if (a.ntiles > 0) {
-        const int gy = (a.H + kChPerWave - 1) / kChPerWave;
-        const int gx = pad_xcd(a.ntiles);
-        // fp32 I/O carries fp64 state: fewer rows in flight keep it in registers
-        constexpr int U = sizeof(A) == 8 ? 2 : 4;
-        hipLaunchKernelGGL((backward_kernel<E, K, U>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+    if (a.N > 0 && a.total_T > 0) {
+        const Tiling t = backward_tiling<E, K>(a.total_T, a.N, a.H);
+        a.sub = t.sub;
+        a.ntiles = (int)t.ntiles;
+        const int gy = WgLayout<LFM2SC_BWD_TW>::groups(a.H);
+        hipLaunchKernelGGL((backward_kernel<E, K, bwd_unroll<E>()>), dim3(pad_xcd(a.ntiles), gy), dim3(kThreads),
+                           LFM2SC_BWD_LDS, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+    } else {
+        a.ntiles = 0;
     }
     const int64_t HK = (int64_t)a.H * K;
     hipLaunchKernelGGL((dw_finish_kernel<A>), dim3((unsigned)((HK + kFinCols - 1) / kFinCols)),
                        dim3(kFinCols * kFinRows), 0, s, (const A*)a.partial, (int64_t)a.ntiles, HK, a.dW);
     return hipGetLastError();
+}
+
+template <typename E>
+static int64_t partial_rows_e(int K, int64_t total_T, int N, int H) {
+    switch (K) {
+        case 1: return backward_tiling<E, 1>(total_T, N, H).ntiles;
+        case 2: return backward_tiling<E, 2>(total_T, N, H).ntiles;
+        case 3: return backward_tiling<E, 3>(total_T, N, H).ntiles;
+        case 4: return backward_tiling<E, 4>(total_T, N, H).ntiles;
+    }
+    return 0;
+}
+
+int64_t backward_partial_rows(int dtype_is_f32, int H, int K, int64_t total_T, int N) {
+    if (N <= 0 || total_T <= 0) return 0;
+    return dtype_is_f32 ? partial_rows_e<float>(K, total_T, N, H) : partial_rows_e<uint16_t>(K, total_T, N, H);
 }
 
 int backward_partial_bytes(int dtype_is_f32) { return dtype_is_f32 ? (int)sizeof(double) : (int)sizeof(float); }

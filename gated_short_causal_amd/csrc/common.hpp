@@ -14,6 +14,44 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef LFM2SC_ROUNDS
+#define LFM2SC_ROUNDS 1        // ragged grids are sized to this many full rounds of resident workgroups
+#endif
+#ifndef LFM2SC_SUB_MIN
+#define LFM2SC_SUB_MIN 8       // shortest per-wave token window
+#endif
+#ifndef LFM2SC_FWD_U
+#define LFM2SC_FWD_U 12        // token rows of loads in flight per wave (forward)
+#endif
+#ifndef LFM2SC_FWD_PIPE
+#define LFM2SC_FWD_PIPE 0      // forward: issue the next batch of rows before consuming the current one
+#endif
+#ifndef LFM2SC_BWD_PIPE
+#define LFM2SC_BWD_PIPE 0      // same for the backward
+#endif
+#ifndef LFM2SC_FWD_TW
+#define LFM2SC_FWD_TW 4        // forward workgroup: waves along time (4: 4 consecutive windows of one 512-channel
+#endif                         // group; 1: one window across 4 x 512 channels)
+#ifndef LFM2SC_BWD_TW
+#define LFM2SC_BWD_TW 4        // same for the backward
+#endif
+#ifndef LFM2SC_FWD_LDS
+#define LFM2SC_FWD_LDS 82944   // dynamic LDS bytes reserved per forward workgroup: more than half of a CU's
+#endif                         // 160 KiB, so one workgroup (4 long row streams) runs per CU
+#ifndef LFM2SC_BWD_LDS
+#define LFM2SC_BWD_LDS 82944   // same for the backward (its static LDS stays within 160 KiB with it)
+#endif
+#ifndef LFM2SC_BWD_U
+#define LFM2SC_BWD_U 3         // token rows of loads in flight per wave (backward, bf16 I/O)
+#endif
+#ifndef LFM2SC_FWD_NT
+#define LFM2SC_FWD_NT 1        // non-temporal hints on streamed rows, forward: 1 = loads, 2 = stores, 3 = both
+#endif
+#ifndef LFM2SC_BWD_NT
+#define LFM2SC_BWD_NT 3        // same for the backward
+#endif
+
 namespace lfm2sc {
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -23,6 +61,7 @@ constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kWavesPerBlock = kThreads / kWave;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element traits
@@ -72,6 +111,24 @@ __device__ __forceinline__ Raw8<E> ld8(const E* p) {
     return r;
 }
 
+// Streamed rows (in_proj, dy, y, d_in): touched once, optionally hinted
+// non-temporal so they do not evict reused data (halo rows, state, weights).
+template <typename E, int NT>
+__device__ __forceinline__ Raw8<E> ld8s(const E* p) {
+    if constexpr ((NT & 1) != 0) {
+    Raw8<E> r;
+    const u32x4* q = reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) {
+        const u32x4 v = __builtin_nontemporal_load(q + i);
+        r.c[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return r;
+    } else {
+        return ld8<E>(p);
+    }
+}
+
 template <typename E>
 __device__ __forceinline__ void st8(E* p, const Raw8<E>& r) {
     uint4* q = reinterpret_cast<uint4*>(p);
@@ -93,8 +150,24 @@ template <> __device__ __forceinline__ Raw8<float> from_f32<float>(const float* 
     return r;
 }
 
+template <typename E, int NT>
+__device__ __forceinline__ void st8s(E* p, const Raw8<E>& r) {
+    if constexpr ((NT & 2) != 0) {
+    u32x4* q = reinterpret_cast<u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) {
+        const u32x4 v = {r.c[i].x, r.c[i].y, r.c[i].z, r.c[i].w};
+        __builtin_nontemporal_store(v, q + i);
+    }
+    } else {
+        st8<E>(p, r);
+    }
+}
+
 template <typename E> __device__ __forceinline__ void load_f32x8(const E* p, float* f) { to_f32(ld8<E>(p), f); }
 template <typename E> __device__ __forceinline__ void store_f32x8(E* p, const float* f) { st8<E>(p, from_f32<E>(f)); }
+template <typename E, int NT>
+__device__ __forceinline__ void store_f32x8s(E* p, const float* f) { st8s<E, NT>(p, from_f32<E>(f)); }
 
 // 8*K contiguous elements (a lane's state block) <-> float s[8][K].
 template <typename E, int K>
@@ -123,6 +196,42 @@ __device__ __forceinline__ void store_block(E* p, const float (&s)[kChPerLane][K
 // everything derived from it -- window bounds, row offsets, loop counts --
 // stays in SGPRs and addresses become scalar base + per-lane offset.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
+
+// ---------------------------------------------------------------- buffer access to streamed rows
+// A streamed row (in_proj, dy, y, d_in) is addressed through a raw buffer
+// descriptor built on the (wave-uniform) row start, with num_records = the
+// row's width in bytes, plus a 32-bit per-lane byte offset.  The descriptor
+// lives in SGPRs, so a load costs no VGPRs for its address, and the hardware
+// range check turns any access past the row into a zero read / dropped write.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferWord3 = 0x00020000;   // gfx9-family raw (untyped) buffer
+
+__device__ __forceinline__ rsrc_t row_rsrc(const void* row, uint32_t row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, (int)row_bytes, kRawBufferWord3);
+}
+
+template <typename E, int NT>
+__device__ __forceinline__ Raw8<E> bld8(rsrc_t r, uint32_t voff) {
+    Raw8<E> out;
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u * i, 0, (NT & 1) ? 2 : 0);
+        out.c[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return out;
+}
+
+template <typename E, int NT>
+__device__ __forceinline__ void bst8(rsrc_t r, uint32_t voff, const Raw8<E>& v) {
+#pragma unroll
+    for (int i = 0; i < Elem<E>::kChunks; ++i) {
+        const u32x4 w = {v.c[i].x, v.c[i].y, v.c[i].z, v.c[i].w};
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, voff + 16u * i, 0, (NT & 2) ? 2 : 0);
+    }
+}
+
+template <typename E, int NT>
+__device__ __forceinline__ void bst8f(rsrc_t r, uint32_t voff, const float* f) { bst8<E, NT>(r, voff, from_f32<E>(f)); }
 
 // ---------------------------------------------------------------- XCD-aware block order
 // MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each
@@ -172,5 +281,49 @@ __device__ __forceinline__ bool find_span(const int32_t* __restrict__ cu, int N,
 }
 
 __device__ __forceinline__ bool slot_ok(int64_t slot, int64_t num_slots) { return slot >= 0 && slot < num_slots; }
+
+// Window length for a ragged launch.  Every window of `kWavesPerBlock * sub`
+// virtual positions is one workgroup per channel group; the grid holds
+// ceil(total_T / gap) + N windows per group.  The windows are sized so that
+// the whole grid is LFM2SC_ROUNDS full rounds of the workgroups the device
+// keeps resident (`resident`, from the occupancy of the kernel): a partial
+// last round would leave most CUs idle while it drains.
+struct Tiling { int sub; int64_t ntiles; };
+
+// A workgroup is TW waves along time (consecutive windows of `sub` tokens) by
+// kWavesPerBlock / TW waves along channels (512 channels each).
+template <int TW>
+struct WgLayout {
+    static_assert(TW == 1 || TW == 2 || TW == 4, "waves along time must divide the workgroup");
+    static constexpr int kCW = kWavesPerBlock / TW;
+    static constexpr int kChPerBlock = kCW * kChPerWave;
+    static int groups(int H) { return (H + kChPerBlock - 1) / kChPerBlock; }
+};
+
+inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, int tw) {
+    const int64_t slots = (int64_t)resident * LFM2SC_ROUNDS / (groups > 0 ? groups : 1);
+    const int64_t free = slots - N;
+    const int64_t denom = (int64_t)tw * (free >= 1 ? free : (slots > 0 ? slots : 1));
+    int64_t sub = (total_T + denom - 1) / denom;
+    if (sub < LFM2SC_SUB_MIN) sub = LFM2SC_SUB_MIN;
+    if (sub > (1 << 24)) sub = 1 << 24;
+    const int64_t gap = sub * tw;
+    return Tiling{(int)sub, (total_T + gap - 1) / gap + N};
+}
+
+// Workgroups of `kernel` (kThreads wide, no dynamic LDS) resident on the
+// current device at once; a conservative default if the query fails.
+template <typename KernelT>
+inline int resident_workgroups(KernelT kernel, size_t dyn_lds = 0) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, dyn_lds) != hipSuccess || cus <= 0 ||
+        per <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus * per;
+}
 
 }  // namespace lfm2sc

@@ -19,7 +19,7 @@ namespace lfm2sc {
 template <typename E, int K>
 __device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, const Raw8<E>& rx,
                                           const float (&wf)[kChPerLane][K],
-                                          float (&hist)[kChPerLane][K > 1 ? K - 1 : 1], E* yp) {
+                                          float (&hist)[kChPerLane][K > 1 ? K - 1 : 1], rsrc_t yrow, uint32_t yoff) {
     float b[8], c[8], x[8], yv[8];
     to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
 #pragma unroll
@@ -35,7 +35,7 @@ __device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, 
             hist[ch][K - 2] = bx;
         }
     }
-    store_f32x8<E>(yp, yv);
+    bst8f<E, LFM2SC_FWD_NT>(yrow, yoff, yv);
 }
 
 // ------------------------------------------------------------------ prefill
@@ -52,14 +52,15 @@ __device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, 
 // B, xv rows of the sequence's last K tokens.  No other wave touches the slot.
 template <typename E, int K, int U>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> a) {
+    using Lay = WgLayout<LFM2SC_FWD_TW>;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
-    const int ch0 = (blockIdx.y * kWave + lane) * kChPerLane;
+    const int ch0 = ((blockIdx.y * Lay::kCW + wave / LFM2SC_FWD_TW) * kWave + lane) * kChPerLane;
     if (ch0 >= a.H) return;
-    const int64_t gap = (int64_t)a.sub * kWavesPerBlock;
-    const int64_t v0 = (int64_t)tile * gap + (int64_t)wave * a.sub;
+    const int64_t gap = (int64_t)a.sub * LFM2SC_FWD_TW;
+    const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % LFM2SC_FWD_TW) * a.sub;
     SeqSpan sp;
     if (!find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) return;
     int64_t lo = sp.lo, hi = sp.hi;
@@ -113,25 +114,83 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
         }
     }
 
-    E* ybase = a.y + ch0;
+    // Streamed rows through buffer descriptors: per-lane byte offsets of this
+    // lane's 8 channels in the B, C and xv blocks of an in_proj row and in a y row.
+    const uint32_t offB = (uint32_t)ch0 * sizeof(E);
+    const uint32_t offC = offB + (uint32_t)H * sizeof(E);
+    const uint32_t offX = offB + 2u * (uint32_t)H * sizeof(E);
+    const uint32_t in_row_bytes = 3u * (uint32_t)H * sizeof(E);
+    const uint32_t y_row_bytes = (uint32_t)H * sizeof(E);
+    const E* in_rows = a.in + sp.r0 * a.in_stride;
+    E* y_rows = a.y + sp.r0 * a.y_stride;
     int64_t t = lo;
+    // Rows in flight: batches of U rows.  With LFM2SC_FWD_PIPE the next batch
+    // is issued before the current one is consumed (two register stages), so
+    // a wave never leaves its memory pipe idle while it computes.
+    auto load_batch = [&](Raw8<E> (&rb)[U], Raw8<E> (&rc)[U], Raw8<E> (&rx)[U], int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const rsrc_t row = row_rsrc(in_rows + (t0 + u) * a.in_stride, in_row_bytes);
+            rb[u] = bld8<E, LFM2SC_FWD_NT>(row, offB);
+            rc[u] = bld8<E, LFM2SC_FWD_NT>(row, offC);
+            rx[u] = bld8<E, LFM2SC_FWD_NT>(row, offX);
+        }
+    };
+    auto use_batch = [&](const Raw8<E> (&rb)[U], const Raw8<E> (&rc)[U], const Raw8<E> (&rx)[U], int64_t t0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, row_rsrc(y_rows + (t0 + u) * a.y_stride, y_row_bytes), offB);
+    };
+#if LFM2SC_FWD_PIPE
+    if (t + U <= hi) {
+        Raw8<E> ab[U], ac[U], ax[U], bb[U], bc[U], bxr[U];
+        load_batch(ab, ac, ax, t);
+        while (true) {
+            if (t + 2 * U <= hi) {
+                load_batch(bb, bc, bxr, t + U);
+                use_batch(ab, ac, ax, t);
+                t += U;
+            } else {
+                use_batch(ab, ac, ax, t);
+                t += U;
+                break;
+            }
+            if (t + 2 * U <= hi) {
+                load_batch(ab, ac, ax, t + U);
+                use_batch(bb, bc, bxr, t);
+                t += U;
+            } else {
+                use_batch(bb, bc, bxr, t);
+                t += U;
+                break;
+            }
+        }
+    }
+#else
     for (; t + U <= hi; t += U) {
+        Raw8<E> rb[U], rc[U], rx[U];
+        load_batch(rb, rc, rx, t);
+        use_batch(rb, rc, rx, t);
+    }
+#endif
+    // Remainder (< U rows): one partial batch, all its loads issued together.
+    if (t < hi) {
+        const int n = (int)(hi - t);
         Raw8<E> rb[U], rc[U], rx[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const E* row = base + (sp.r0 + t + u) * a.in_stride;
-            rb[u] = ld8<E>(row);
-            rc[u] = ld8<E>(row + H);
-            rx[u] = ld8<E>(row + 2 * H);
+            if (u < n) {
+                const rsrc_t row = row_rsrc(in_rows + (t + u) * a.in_stride, in_row_bytes);
+                rb[u] = bld8<E, LFM2SC_FWD_NT>(row, offB);
+                rc[u] = bld8<E, LFM2SC_FWD_NT>(row, offC);
+                rx[u] = bld8<E, LFM2SC_FWD_NT>(row, offX);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, ybase + (sp.r0 + t + u) * a.y_stride);
-    }
-    for (; t < hi; ++t) {
-        const E* row = base + (sp.r0 + t) * a.in_stride;
-        fwd_token<E, K>(ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H), wf, hist,
-                        ybase + (sp.r0 + t) * a.y_stride);
+            if (u < n)
+                fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, row_rsrc(y_rows + (t + u) * a.y_stride, y_row_bytes),
+                                offB);
     }
 
     if (slotp) {
@@ -275,34 +334,21 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs<E> a,
     st8<E>(a.pool + slot * a.slot_stride + e0, ld8<E>(src));
 }
 
-// ------------------------------------------------------------------ tiling policy
-// Window length per wave: long enough to amortise the K-1 halo rows, short
-// enough that the grid holds several waves per SIMD (1024 SIMDs on MI355X).
-static int pow2_floor(int64_t v) { int p = 1; while ((int64_t)p * 2 <= v) p *= 2; return p; }
-
-int prefill_sub(int64_t total_T, int H) {
-    const int64_t groups = (H + kChPerWave - 1) / kChPerWave;
-    const int64_t target_waves = 8192;
-    int64_t s = total_T * groups / target_waves;
-    int p = pow2_floor(s < 1 ? 1 : s);
-    if (p < 8) p = 8;
-    if (p > 64) p = 64;
-    return p;
-}
-
-int backward_sub(int64_t total_T, int H) { return prefill_sub(total_T, H); }
-
-int64_t ragged_tiles(int64_t total_T, int N, int sub) {
-    const int64_t gap = (int64_t)sub * kWavesPerBlock;
+// ------------------------------------------------------------------ launchers
+int64_t ragged_tiles_bound(int64_t total_T, int N) {
+    const int64_t gap = (int64_t)LFM2SC_SUB_MIN;
     return (total_T + gap - 1) / gap + N;
 }
 
-// ------------------------------------------------------------------ launchers
 template <typename E, int K>
-static hipError_t prefill_k(const PrefillArgs<E>& a, hipStream_t s) {
-    const int gy = (a.H + kChPerWave - 1) / kChPerWave;
-    const int gx = pad_xcd(a.ntiles);
-    hipLaunchKernelGGL((prefill_kernel<E, K, 8>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+static hipError_t prefill_k(PrefillArgs<E> a, hipStream_t s) {
+    constexpr auto kernel = prefill_kernel<E, K, LFM2SC_FWD_U>;
+    static const int resident = resident_workgroups(kernel, LFM2SC_FWD_LDS);
+    const int gy = WgLayout<LFM2SC_FWD_TW>::groups(a.H);
+    const Tiling t = ragged_tiling(a.total_T, a.N, gy, resident, LFM2SC_FWD_TW);
+    a.sub = t.sub;
+    a.ntiles = (int)t.ntiles;
+    hipLaunchKernelGGL(kernel, dim3(pad_xcd(a.ntiles), gy), dim3(kThreads), LFM2SC_FWD_LDS, s, a);
     return hipGetLastError();
 }
 

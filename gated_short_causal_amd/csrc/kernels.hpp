@@ -16,8 +16,8 @@ struct PrefillArgs {
     E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     E* y; int64_t y_stride;
     int H;
-    int sub;      // tokens per wave window (a workgroup window is 4 * sub)
-    int ntiles;   // number of workgroup windows
+    int sub;      // tokens per wave window (a workgroup window is 4 * sub); set by the launcher
+    int ntiles;   // number of workgroup windows; set by the launcher
 };
 
 template <typename E>
@@ -61,11 +61,13 @@ struct BackwardArgs {
     int ntiles;
 };
 
-// Tiling policy shared by the launchers and the workspace-size query.
-int prefill_sub(int64_t total_T, int H);
-int backward_sub(int64_t total_T, int H);
-int64_t ragged_tiles(int64_t total_T, int N, int sub);
-int backward_partial_bytes(int dtype_is_f32);   // bytes per dW partial element
+// Rows of dW partials (one per workgroup window) a backward launch of these
+// sizes writes to its workspace, and the bytes of one partial element; the
+// launcher and the workspace-size query share this.
+int64_t backward_partial_rows(int dtype_is_f32, int H, int K, int64_t total_T, int N);
+int backward_partial_bytes(int dtype_is_f32);
+// Upper bound on ragged windows for any tiling (host-side size checks).
+int64_t ragged_tiles_bound(int64_t total_T, int N);
 
 template <typename E> hipError_t launch_prefill(const PrefillArgs<E>& a, int K, hipStream_t s);
 template <typename E> hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s);

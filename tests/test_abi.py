@@ -167,10 +167,11 @@ def test_workspace_bytes(L):
     assert f(0, 2048, 3, 0, 0) == 0
     assert f(0, 2048, 3, 65536, 1) > 0
     assert f(0, 2048, 3, 65536, 1) % 256 == 0
-    # partial rows of H*K fp32 values: grows with tokens and with sequences
+    # whole partial rows of H*K fp32 values (fp64 for fp32 I/O); never fewer for more tokens or sequences
     assert f(0, 2048, 3, 65536, 1) >= 2048 * 3 * 4
     assert f(0, 2048, 3, 65536, 8) >= f(0, 2048, 3, 65536, 1)
-    assert f(0, 2048, 3, 1 << 20, 1) > f(0, 2048, 3, 65536, 1)
+    assert f(0, 2048, 3, 1 << 20, 1) >= f(0, 2048, 3, 65536, 1)
+    assert f(1, 2048, 3, 65536, 1) >= 2 * f(0, 2048, 3, 65536, 1) - 256
     assert f(9, 2048, 3, 64, 1) == 0 and f(0, 12, 3, 64, 1) == 0 and f(0, 2048, 5, 64, 1) == 0
 
 
