@@ -117,53 +117,67 @@ def timed_loop(fn, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def extra_measurements(wl_mod, g, steps):
-    """Decode, ragged prefill and verify at their LFM2-1.2B shapes, rotating input sets past the 256 MB
-    Infinity Cache so the numbers are HBM numbers (host launch overhead included for the tiny calls)."""
+def graph_time(calls, replays):
+    """GPU time per call with host launch overhead removed: the calls are captured once into a HIP graph
+    (torch.cuda.CUDAGraph; the library launches on the capturing stream) and the graph is replayed."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (replays * len(calls))
+
+
+def extra_measurements(wl_mod, steps):
+    """Decode, ragged prefill and verify at their LFM2-1.2B shapes.  Input sets are rotated so that one pass
+    touches more than 2 x 256 MB (past the Infinity Cache): these are HBM figures.  `ms` is GPU time per call
+    from graph replay; `eager_ms` is the back-to-back eager rate, which includes host launch overhead."""
     import torch
     from gated_short_causal_amd import lfm2sc_decode_step, lfm2sc_prefill_ragged, lfm2sc_verify_window
     dev = torch.device("cuda")
     out = {}
-    # decode: 10.5 MB per call, 64 rotated sets
+
+    def record(name, calls, nbytes):
+        eager = timed_loop(lambda: [c() for c in calls], steps, 2) / len(calls)
+        ms = graph_time(calls, steps)
+        out[name] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1), "pct_of_hbm_peak":
+                     round(100 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 1), "eager_ms": round(eager, 5), "bytes": int(nbytes)}
+
+    # decode: 10.5 MB per call, 64 rotated sets (672 MB)
     sets = [wl_mod.decode_lfm2(seed=200 + i).to(dev) for i in range(64)]
     ys = [torch.empty(256, 2048, dtype=torch.bfloat16, device=dev) for _ in sets]
-    i = [0]
-
-    def dec():
-        s = sets[i[0] % 64]
-        lfm2sc_decode_step(s.inp, s.w, s.pool, s.slot_idx, ys[i[0] % 64])
-        i[0] += 1
-    ms = timed_loop(dec, steps * 64, 64)
-    b = algo_bytes_decode(256, 2048, 3, 2)
-    out["decode_N256"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
-    del sets, ys
-    # ragged prefill: ~138 MB per call, 5 rotated sets
+    calls = [(lambda s=s, y=y: lfm2sc_decode_step(s.inp, s.w, s.pool, s.slot_idx, y)) for s, y in zip(sets, ys)]
+    record("decode_N256", calls, algo_bytes_decode(256, 2048, 3, 2))
+    del sets, ys, calls
+    # ragged prefill: ~141 MB per call, 5 rotated sets (705 MB)
     sets = [wl_mod.ragged_prefill_lfm2(seed=300 + i).to(dev) for i in range(5)]
     ys = [torch.empty(s.inp.shape[0], 2048, dtype=torch.bfloat16, device=dev) for s in sets]
-    j = [0]
-
-    def pre():
-        s = sets[j[0] % 5]
-        lfm2sc_prefill_ragged(s.inp, s.cu, s.w, ys[j[0] % 5], s.pool, s.slot_idx)
-        j[0] += 1
-    ms = timed_loop(pre, steps * 5, 5)
-    b = sum(algo_bytes_prefill(s.inp.shape[0], 8, 2048, 3, 2) for s in sets) / len(sets)
-    out["ragged_prefill_N8"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": int(b)}
-    del sets, ys
-    # verify: 15.5 MB per call, 48 rotated sets
+    calls = [(lambda s=s, y=y: lfm2sc_prefill_ragged(s.inp, s.cu, s.w, y, s.pool, s.slot_idx)) for s, y in zip(sets, ys)]
+    record("ragged_prefill_N8", calls, sum(algo_bytes_prefill(s.inp.shape[0], 8, 2048, 3, 2) for s in sets) / len(sets))
+    del sets, ys, calls
+    # verify: 15.5 MB per call, 48 rotated sets (743 MB)
     sets = [wl_mod.verify_lfm2(seed=400 + i).to(dev) for i in range(48)]
     outs = [(torch.empty(512, 2048, dtype=torch.bfloat16, device=dev),
              torch.empty(64, 8, 2048, 3, dtype=torch.bfloat16, device=dev)) for _ in sets]
-    k = [0]
-
-    def ver():
-        s = sets[k[0] % 48]
-        y, win = outs[k[0] % 48]
-        lfm2sc_verify_window(s.inp, s.w, s.pool, s.slot_idx, 8, win, y)
-        k[0] += 1
-    ms = timed_loop(ver, steps * 48, 48)
-    b = algo_bytes_verify(64, 8, 2048, 3, 2)
-    out["verify_64x8"] = {"ms": round(ms, 5), "GB/s": round(b / ms / 1e6, 1), "bytes": b}
+    calls = [(lambda s=s, o=o: lfm2sc_verify_window(s.inp, s.w, s.pool, s.slot_idx, 8, o[1], o[0]))
+             for s, o in zip(sets, outs)]
+    record("verify_64x8", calls, algo_bytes_verify(64, 8, 2048, 3, 2))
     return out
 
 
@@ -273,7 +287,7 @@ def main():
         "context": {"pages_mi325x_liger_fwd_bwd_ms": {"T=4096": 0.463, "T=65536": 8.083}},
     }
     if args.extra:
-        line["extra"] = extra_measurements(wl, None, max(1, args.steps // 4))
+        line["extra"] = extra_measurements(wl, max(2, args.steps // 2))
     if not args.no_cpu:
         print("bench: timing the oracle CPU baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, T, H, K, args.cpu_channels)

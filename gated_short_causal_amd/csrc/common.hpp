@@ -59,6 +59,7 @@ constexpr int kChPerLane = 8;      // channels per lane
 constexpr int kChPerWave = kWave * kChPerLane;   // 512
 constexpr int kThreads = 256;      // 4 waves per workgroup
 constexpr int kWavesPerBlock = kThreads / kWave;
+constexpr int kSmallBlock = kWave;   // decode / verify / commit: one wave per workgroup, spread over every CU
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

@@ -223,9 +223,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
 // of a lane is independent of the others except the state, whose address
 // needs the (wave-uniform, scalar-loaded) slot index.
 template <typename E, int K>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs<E> a) {
+__global__ __launch_bounds__(kSmallBlock) void decode_kernel(const DecodeArgs<E> a) {
     const int i = blockIdx.x;
-    const int ch0 = (blockIdx.y * kThreads + threadIdx.x) * kChPerLane;
+    const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
     if (ch0 >= a.H) return;
     const int H = a.H;
     const int64_t slot = a.slot_idx[i];
@@ -264,9 +264,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const DecodeArgs<E> a)
 // L draft tokens per sequence from the slot state (read only); after each
 // token the lane's 8 x K window goes to the tape windows[i][s].
 template <typename E, int K, int U>
-__global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs<E> a) {
+__global__ __launch_bounds__(kSmallBlock) void verify_kernel(const VerifyArgs<E> a) {
     const int i = blockIdx.x;
-    const int ch0 = (blockIdx.y * kThreads + threadIdx.x) * kChPerLane;
+    const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
     if (ch0 >= a.H) return;
     const int H = a.H;
     const int64_t HK = (int64_t)H * K;
@@ -322,9 +322,9 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(const VerifyArgs<E> a)
 // pool[slot[i]] <- windows[i][accept[i]-1] for accept[i] in [1, L]: a plain
 // 16-byte-per-lane copy of the accepted [H, K] window.
 template <typename E>
-__global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs<E> a, int64_t HK) {
+__global__ __launch_bounds__(kSmallBlock) void commit_kernel(const CommitArgs<E> a, int64_t HK) {
     const int i = blockIdx.x;
-    const int64_t e0 = ((int64_t)blockIdx.y * kThreads + threadIdx.x) * 8;
+    const int64_t e0 = ((int64_t)blockIdx.y * kSmallBlock + threadIdx.x) * 8;
     if (e0 >= HK) return;
     const int acc = a.accept[i];
     if (acc < 1 || acc > a.L) return;
@@ -366,7 +366,8 @@ hipError_t launch_prefill(const PrefillArgs<E>& a, int K, hipStream_t s) {
 template <typename E, int K>
 static hipError_t decode_k(const DecodeArgs<E>& a, hipStream_t s) {
     const int lanes = a.H / kChPerLane;
-    hipLaunchKernelGGL((decode_kernel<E, K>), dim3(a.N, (lanes + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((decode_kernel<E, K>), dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock), 0,
+                       s, a);
     return hipGetLastError();
 }
 
@@ -384,7 +385,8 @@ hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s) {
 template <typename E, int K>
 static hipError_t verify_k(const VerifyArgs<E>& a, hipStream_t s) {
     const int lanes = a.H / kChPerLane;
-    hipLaunchKernelGGL((verify_kernel<E, K, 4>), dim3(a.N, (lanes + kThreads - 1) / kThreads), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((verify_kernel<E, K, 4>), dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock),
+                       0, s, a);
     return hipGetLastError();
 }
 
@@ -403,8 +405,8 @@ template <typename E>
 hipError_t launch_commit(const CommitArgs<E>& a, int K, hipStream_t s) {
     const int64_t HK = (int64_t)a.H * K;
     const int64_t lanes = HK / 8;
-    hipLaunchKernelGGL((commit_kernel<E>), dim3(a.N, (unsigned)((lanes + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       a, HK);
+    hipLaunchKernelGGL((commit_kernel<E>), dim3(a.N, (unsigned)((lanes + kSmallBlock - 1) / kSmallBlock)),
+                       dim3(kSmallBlock), 0, s, a, HK);
     return hipGetLastError();
 }
 
