@@ -165,6 +165,12 @@ def extra_measurements(wl_mod, steps):
     calls = [(lambda s=s, y=y: lfm2sc_decode_step(s.inp, s.w, s.pool, s.slot_idx, y)) for s, y in zip(sets, ys)]
     record("decode_N256", calls, algo_bytes_decode(256, 2048, 3, 2))
     del sets, ys, calls
+    # decode at a larger batch (N=4096 of a 8192-slot pool, 168 MB per call, 4 rotated sets): launch latency amortised
+    sets = [wl_mod.decode_lfm2(seed=250 + i, N=4096, slots=8192).to(dev) for i in range(4)]
+    ys = [torch.empty(4096, 2048, dtype=torch.bfloat16, device=dev) for _ in sets]
+    calls = [(lambda s=s, y=y: lfm2sc_decode_step(s.inp, s.w, s.pool, s.slot_idx, y)) for s, y in zip(sets, ys)]
+    record("decode_N4096", calls, algo_bytes_decode(4096, 2048, 3, 2))
+    del sets, ys, calls
     # ragged prefill: ~141 MB per call, 5 rotated sets (705 MB)
     sets = [wl_mod.ragged_prefill_lfm2(seed=300 + i).to(dev) for i in range(5)]
     ys = [torch.empty(s.inp.shape[0], 2048, dtype=torch.bfloat16, device=dev) for s in sets]

@@ -213,40 +213,12 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
                       bld8<E, LFM2SC_BWD_NT>(ir, o.c), bld8<E, LFM2SC_BWD_NT>(ir, o.x), din_row(r), false, din_row(r),
                       o);
     }
-    // Steady state: batches of U rows of loads in flight (two register stages
-    // with LFM2SC_BWD_PIPE, so the next batch is issued before this one is used).
-#if LFM2SC_BWD_PIPE
-    if (r + U <= hi) {
-        Raw8<E> ady[U], ab[U], ac[U], ax[U], bdy[U], bb[U], bc[U], bxr[U];
-        load_batch(ady, ab, ac, ax, r);
-        while (true) {
-            if (r + 2 * U <= hi) {
-                load_batch(bdy, bb, bc, bxr, r + U);
-                use_batch(ady, ab, ac, ax, r);
-                r += U;
-            } else {
-                use_batch(ady, ab, ac, ax, r);
-                r += U;
-                break;
-            }
-            if (r + 2 * U <= hi) {
-                load_batch(ady, ab, ac, ax, r + U);
-                use_batch(bdy, bb, bc, bxr, r);
-                r += U;
-            } else {
-                use_batch(bdy, bb, bc, bxr, r);
-                r += U;
-                break;
-            }
-        }
-    }
-#else
+    // Steady state: batches of U rows, all loads of a batch issued together.
     for (; r + U <= hi; r += U) {
         Raw8<E> rdy[U], rb[U], rc[U], rx[U];
         load_batch(rdy, rb, rc, rx, r);
         use_batch(rdy, rb, rc, rx, r);
     }
-#endif
     // Remainder (< U rows): one partial batch, all its loads issued together.
     if (r < hi) {
         const int n = (int)(hi - r);

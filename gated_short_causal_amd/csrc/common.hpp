@@ -24,12 +24,6 @@
 #ifndef LFM2SC_FWD_U
 #define LFM2SC_FWD_U 12        // token rows of loads in flight per wave (forward)
 #endif
-#ifndef LFM2SC_FWD_PIPE
-#define LFM2SC_FWD_PIPE 0      // forward: issue the next batch of rows before consuming the current one
-#endif
-#ifndef LFM2SC_BWD_PIPE
-#define LFM2SC_BWD_PIPE 0      // same for the backward
-#endif
 #ifndef LFM2SC_FWD_TW
 #define LFM2SC_FWD_TW 4        // forward workgroup: waves along time (4: 4 consecutive windows of one 512-channel
 #endif                         // group; 1: one window across 4 x 512 channels)

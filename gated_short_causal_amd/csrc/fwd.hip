@@ -84,6 +84,22 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
         if (slot_ok(slot, a.num_slots)) slotp = a.pool + slot * a.slot_stride + (int64_t)ch0 * K;
     }
 
+    // The owner's final state needs bx of the sequence's last K tokens: those
+    // loads are independent of everything else, so they are issued here, at the
+    // window start, instead of costing an extra round trip after the last batch.
+    Raw8<E> fin_b[K], fin_x[K];
+    if (slotp) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t j = sp.T + k;   // index in the padded history [state | bx...]
+            if (j >= K) {
+                const E* row = base + (sp.r0 + j - K) * a.in_stride;
+                fin_b[k] = ld8<E>(row);
+                fin_x[k] = ld8<E>(row + 2 * H);
+            }
+        }
+    }
+
     float hist[kChPerLane][K > 1 ? K - 1 : 1];
     if constexpr (K > 1) {
         if (owner) {
@@ -124,9 +140,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
     const E* in_rows = a.in + sp.r0 * a.in_stride;
     E* y_rows = a.y + sp.r0 * a.y_stride;
     int64_t t = lo;
-    // Rows in flight: batches of U rows.  With LFM2SC_FWD_PIPE the next batch
-    // is issued before the current one is consumed (two register stages), so
-    // a wave never leaves its memory pipe idle while it computes.
+    // Rows in flight: batches of U rows, all loads of a batch issued together.
     auto load_batch = [&](Raw8<E> (&rb)[U], Raw8<E> (&rc)[U], Raw8<E> (&rx)[U], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -141,38 +155,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
         for (int u = 0; u < U; ++u)
             fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, row_rsrc(y_rows + (t0 + u) * a.y_stride, y_row_bytes), offB);
     };
-#if LFM2SC_FWD_PIPE
-    if (t + U <= hi) {
-        Raw8<E> ab[U], ac[U], ax[U], bb[U], bc[U], bxr[U];
-        load_batch(ab, ac, ax, t);
-        while (true) {
-            if (t + 2 * U <= hi) {
-                load_batch(bb, bc, bxr, t + U);
-                use_batch(ab, ac, ax, t);
-                t += U;
-            } else {
-                use_batch(ab, ac, ax, t);
-                t += U;
-                break;
-            }
-            if (t + 2 * U <= hi) {
-                load_batch(ab, ac, ax, t + U);
-                use_batch(bb, bc, bxr, t);
-                t += U;
-            } else {
-                use_batch(bb, bc, bxr, t);
-                t += U;
-                break;
-            }
-        }
-    }
-#else
     for (; t + U <= hi; t += U) {
         Raw8<E> rb[U], rc[U], rx[U];
         load_batch(rb, rc, rx, t);
         use_batch(rb, rc, rx, t);
     }
-#endif
     // Remainder (< U rows): one partial batch, all its loads issued together.
     if (t < hi) {
         const int n = (int)(hi - t);
@@ -206,10 +193,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
 #pragma unroll
                 for (int c = 0; c < 8; ++c) fin[c][k] = s0[c][j];
             } else {
-                const E* row = base + (sp.r0 + j - K) * a.in_stride;
                 float b[8], x[8];
-                load_f32x8<E>(row, b);
-                load_f32x8<E>(row + 2 * H, x);
+                to_f32(fin_b[k], b);
+                to_f32(fin_x[k], x);
 #pragma unroll
                 for (int c = 0; c < 8; ++c) fin[c][k] = b[c] * x[c];
             }
@@ -385,7 +371,7 @@ hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s) {
 template <typename E, int K>
 static hipError_t verify_k(const VerifyArgs<E>& a, hipStream_t s) {
     const int lanes = a.H / kChPerLane;
-    hipLaunchKernelGGL((verify_kernel<E, K, 4>), dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock),
+    hipLaunchKernelGGL((verify_kernel<E, K, 8>), dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock),
                        0, s, a);
     return hipGetLastError();
 }
