@@ -36,11 +36,12 @@ def _load():
     lib.oracle_set_threads.restype = None
     lib.oracle_get_threads.argtypes = []
     lib.oracle_get_threads.restype = _int
-    lib.oracle_prefill.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _i64, _ip, _dp]
-    lib.oracle_decode.argtypes = [_int, _int, _int, _dp, _i64, _dp, _dp, _i64, _ip, _dp]
-    lib.oracle_verify.argtypes = [_int, _int, _int, _int, _dp, _i64, _dp, _dp, _i64, _ip, _dp, _dp]
+    lib.oracle_prefill.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _dp, _i64, _ip, _dp]
+    lib.oracle_decode.argtypes = [_int, _int, _int, _dp, _i64, _dp, _dp, _dp, _i64, _ip, _dp]
+    lib.oracle_verify.argtypes = [_int, _int, _int, _int, _dp, _i64, _dp, _dp, _dp, _i64, _ip, _dp, _dp]
     lib.oracle_commit.argtypes = [_int, _int, _int, _int, _dp, _ip, _dp, _i64, _ip]
-    lib.oracle_backward.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _i64, _ip, _dp, _dp, _dp]
+    lib.oracle_backward.argtypes = [_int, _int, _i64, _dp, _i64, _ip, _int, _dp, _dp, _dp, _i64, _ip, _dp, _dp, _dp,
+                                    _dp, _dp, _dp]
     for name in ("oracle_prefill", "oracle_decode", "oracle_verify", "oracle_commit", "oracle_backward"):
         getattr(lib, name).restype = _int
     _lib = lib
@@ -88,9 +89,9 @@ def _pool3(pool, H, K):
     return np.ascontiguousarray(p).reshape(-1, H, K).copy()
 
 
-def prefill(inp, cu, w, pool=None, slot_idx=None):
+def prefill(inp, cu, w, pool=None, slot_idx=None, bias=None):
     """Ragged prefill.  Returns (y [total_T, H], new_pool or None)."""
-    inp, w, cu = f64(inp), f64(w), i32(cu)
+    inp, w, cu, bias = f64(inp), f64(w), i32(cu), f64(bias)
     H, K = w.shape
     total_T = inp.shape[0]
     N = cu.shape[0] - 1
@@ -100,35 +101,35 @@ def prefill(inp, cu, w, pool=None, slot_idx=None):
     if pool is not None:
         newpool = _pool3(pool, H, K)
         sl = i32(slot_idx)
-    _check(_load().oracle_prefill(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w),
+    _check(_load().oracle_prefill(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w), _p(bias),
                                   _p(newpool), 0 if newpool is None else newpool.shape[0],
                                   _p(sl, _ip), _p(y)), "prefill")
     return y, newpool
 
 
-def decode(inp, w, pool, slot_idx):
+def decode(inp, w, pool, slot_idx, bias=None):
     """One decode token per sequence (row i = sequence i).  Returns (y [N, H], new_pool)."""
-    inp, w = f64(inp), f64(w)
+    inp, w, bias = f64(inp), f64(w), f64(bias)
     H, K = w.shape
     sl = i32(slot_idx)
     N = sl.shape[0]
     newpool = _pool3(pool, H, K)
     y = np.full((N, H), np.nan)
-    _check(_load().oracle_decode(H, K, N, _p(inp), inp.shape[1], _p(w), _p(newpool), newpool.shape[0],
+    _check(_load().oracle_decode(H, K, N, _p(inp), inp.shape[1], _p(w), _p(bias), _p(newpool), newpool.shape[0],
                                  _p(sl, _ip), _p(y)), "decode")
     return y, newpool
 
 
-def verify(inp, w, pool, slot_idx, L):
+def verify(inp, w, pool, slot_idx, L, bias=None):
     """Verify window (row i*L+s).  Returns (y [N*L, H], tape [N, L, H, K]); pool untouched."""
-    inp, w = f64(inp), f64(w)
+    inp, w, bias = f64(inp), f64(w), f64(bias)
     H, K = w.shape
     sl = i32(slot_idx)
     N = sl.shape[0]
     p = _pool3(pool, H, K)
     y = np.full((N * L, H), np.nan)
     tape = np.full((N, L, H, K), np.nan)
-    _check(_load().oracle_verify(H, K, N, L, _p(inp), inp.shape[1], _p(w), _p(p), p.shape[0],
+    _check(_load().oracle_verify(H, K, N, L, _p(inp), inp.shape[1], _p(w), _p(bias), _p(p), p.shape[0],
                                  _p(sl, _ip), _p(tape), _p(y)), "verify")
     return y, tape
 
@@ -144,19 +145,23 @@ def commit(tape, accept, pool, slot_idx):
     return newpool
 
 
-def backward(inp, cu, w, dy, pool=None, slot_idx=None):
-    """Backward of prefill.  Returns (d_in [total_T, 3H] = dB|dC|dxv, dW [H, K])."""
-    inp, w, cu, dy = f64(inp), f64(w), i32(cu), f64(dy)
+def backward(inp, cu, w, dy, pool=None, slot_idx=None, bias=None, d_final=None, full=False):
+    """Backward of prefill.  Returns (d_in [total_T, 3H] = dB|dC|dxv, dW [H, K]), or with full=True
+    (d_in, dW, dbias [H], d_init [N, H, K]).  d_final: gradient of each sequence's final state [N, H, K]."""
+    inp, w, cu, dy, bias = f64(inp), f64(w), i32(cu), f64(dy), f64(bias)
     H, K = w.shape
     total_T = inp.shape[0]
     N = cu.shape[0] - 1
+    dF = None if d_final is None else f64(d_final).reshape(N, H, K)
     d_in = np.full((total_T, 3 * H), np.nan)
     dW = np.full((H, K), np.nan)
+    dbias = np.full((H,), np.nan)
+    d_init = np.full((N, H, K), np.nan)
     p, sl = None, None
     if pool is not None:
         p = _pool3(pool, H, K)
         sl = i32(slot_idx)
-    _check(_load().oracle_backward(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w),
-                                   _p(p), 0 if p is None else p.shape[0], _p(sl, _ip), _p(dy),
-                                   _p(d_in), _p(dW)), "backward")
-    return d_in, dW
+    _check(_load().oracle_backward(H, K, total_T, _p(inp), inp.shape[1], _p(cu, _ip), N, _p(w), _p(bias),
+                                   _p(p), 0 if p is None else p.shape[0], _p(sl, _ip), _p(dy), _p(dF),
+                                   _p(d_in), _p(dW), _p(dbias), _p(d_init)), "backward")
+    return (d_in, dW, dbias, d_init) if full else (d_in, dW)

@@ -70,7 +70,7 @@ static int check_slots(const int32_t* slot_idx, int N, int64_t num_slots) {
 int oracle_prefill(int H, int K, int64_t total_T,
                    const double* in, int64_t in_stride,
                    const int32_t* cu, int N,
-                   const double* w,
+                   const double* w, const double* bias,
                    double* pool, int64_t num_slots, const int32_t* slot_idx,
                    double* y) {
     if (H <= 0 || K <= 0 || total_T < 0 || in_stride < 3 * (int64_t)H) return -1;
@@ -103,6 +103,7 @@ int oracle_prefill(int H, int K, int64_t total_T,
                 const double* row = in + (r0 + t) * in_stride;
                 double conv = 0.0;
                 for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * X[t + 1 + k];
+                if (bias) conv += bias[h];
                 y[(r0 + t) * H + h] = row[H + h] * conv;        /* y = C * conv */
             }
             if (fin)
@@ -130,7 +131,7 @@ int oracle_prefill(int H, int K, int64_t total_T,
  */
 int oracle_decode(int H, int K, int N,
                   const double* in, int64_t in_stride,
-                  const double* w,
+                  const double* w, const double* bias,
                   double* pool, int64_t num_slots, const int32_t* slot_idx,
                   double* y) {
     if (H <= 0 || K <= 0 || N < 0 || in_stride < 3 * (int64_t)H) return -1;
@@ -149,6 +150,7 @@ int oracle_decode(int H, int K, int N,
             S[K - 1] = row[h] * row[2 * H + h];                /* append bx      */
             double conv = 0.0;
             for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * S[k];
+            if (bias) conv += bias[h];
             y[(int64_t)i * H + h] = row[H + h] * conv;
         }
     }
@@ -167,7 +169,7 @@ int oracle_decode(int H, int K, int N,
  */
 int oracle_verify(int H, int K, int N, int L,
                   const double* in, int64_t in_stride,
-                  const double* w,
+                  const double* w, const double* bias,
                   const double* pool, int64_t num_slots, const int32_t* slot_idx,
                   double* tape, double* y) {
     if (H <= 0 || K <= 0 || N < 0 || L < 0 || in_stride < 3 * (int64_t)H) return -1;
@@ -189,6 +191,7 @@ int oracle_verify(int H, int K, int N, int L,
                 S[K - 1] = row[h] * row[2 * H + h];
                 double conv = 0.0;
                 for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * S[k];
+                if (bias) conv += bias[h];
                 y[r * H + h] = row[H + h] * conv;
                 for (int k = 0; k < K; ++k) tape[(r * H + h) * K + k] = S[k];
             }
@@ -232,24 +235,28 @@ int oracle_commit(int H, int K, int N, int L,
  * Liger-Kernel PR 1317, section "Kernel changes / Gated short convolution":
  * the op's backward gives the input gradient through the fused B and C gates
  * and a weight gradient with all K taps of a channel together.  The formulas
- * are the derivatives of the forward definition (the pages print none).  With
- * X the padded history used in oracle_prefill, for one channel of one sequence:
- *     conv[t] = sum_k w[k] X[t+1+k],  y[t] = C[t] conv[t],  X[K+u] = B[u] xv[u]
- * so, with g[t] = dy[t] C[t]:
+ * are the chain rule applied to the forward definition (the pages print
+ * none).  With X the padded history used in oracle_prefill, for one channel
+ * of one sequence:
+ *     conv[t] = bias + sum_k w[k] X[t+1+k],  y[t] = C[t] conv[t],
+ *     X[k] = S0[k] (k < K),  X[K+u] = B[u] xv[u],  final state F = X[T .. T+K-1].
+ * With g[t] = dy[t] C[t] the chain rule gives, term by term:
  *     dC[t]  = dy[t] conv[t]
- *     dX[j]  = sum over (t, k) with t+1+k = j of w[k] g[t]
- *     dBx[u] = dX[K+u] = sum_k w[k] g[u+K-1-k]     (terms with 0 <= u+K-1-k < T)
- *     dB[u]  = dBx[u] xv[u],   dxv[u] = dBx[u] B[u]
+ *     dX[j]  = sum over (t, k) with t+1+k = j of w[k] g[t]   (every conv term)
+ *              + dF[j-T] for j >= T                          (the final state)
+ *     dB[u]  = dX[K+u] xv[u],   dxv[u] = dX[K+u] B[u]
+ *     dS0[k] = dX[k]            (k < K)
  *     dW[k]  = sum over sequences and t of g[t] X[t+1+k]
- * No gradient is produced for the initial state.
+ *     dbias  = sum over sequences and t of g[t]
+ * dX is accumulated by scattering each conv term, in token order.
  */
 int oracle_backward(int H, int K, int64_t total_T,
                     const double* in, int64_t in_stride,
                     const int32_t* cu, int N,
-                    const double* w,
+                    const double* w, const double* bias,
                     const double* pool, int64_t num_slots, const int32_t* slot_idx,
-                    const double* dy,
-                    double* d_in, double* dW) {
+                    const double* dy, const double* d_final,
+                    double* d_in, double* dW, double* dbias, double* d_init) {
     if (H <= 0 || K <= 0 || total_T < 0 || in_stride < 3 * (int64_t)H) return -1;
     if (check_cu(cu, N, total_T)) return -1;
     if (pool && check_slots(slot_idx, N, num_slots)) return -1;
@@ -265,8 +272,10 @@ int oracle_backward(int H, int K, int64_t total_T,
 #pragma omp parallel for num_threads(g_threads) schedule(static)
     for (int h = 0; h < H; ++h) {
         double* X = (double*)malloc(sizeof(double) * (size_t)(K + maxT));
-        double* g = (double*)malloc(sizeof(double) * (size_t)(maxT > 0 ? maxT : 1));
-        if (!X || !g) { fail = 1; free(X); free(g); continue; }
+        double* dX = (double*)malloc(sizeof(double) * (size_t)(K + maxT));
+        if (!X || !dX) { fail = 1; free(X); free(dX); continue; }
+        const double b = bias ? bias[h] : 0.0;
+        double db = 0.0;
         for (int k = 0; k < K; ++k) dW[(int64_t)h * K + k] = 0.0;
         for (int i = 0; i < N; ++i) {
             const int64_t r0 = cu[i];
@@ -277,28 +286,33 @@ int oracle_backward(int H, int K, int64_t total_T,
                 const double* row = in + (r0 + u) * in_stride;
                 X[K + u] = row[h] * row[2 * H + h];
             }
+            for (int64_t j = 0; j < K + T; ++j) dX[j] = 0.0;
             for (int64_t t = 0; t < T; ++t) {
                 const double* row = in + (r0 + t) * in_stride;
                 const double dyt = dy[(r0 + t) * H + h];
-                double conv = 0.0;
+                double conv = b;
                 for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * X[t + 1 + k];
-                g[t] = dyt * row[H + h];
+                const double g = dyt * row[H + h];
                 d_in[(r0 + t) * 3 * H + H + h] = dyt * conv;             /* dC */
-                for (int k = 0; k < K; ++k) dW[(int64_t)h * K + k] += g[t] * X[t + 1 + k];
+                for (int k = 0; k < K; ++k) {
+                    dX[t + 1 + k] += w[(int64_t)h * K + k] * g;
+                    dW[(int64_t)h * K + k] += g * X[t + 1 + k];
+                }
+                db += g;
             }
+            if (d_final)
+                for (int k = 0; k < K; ++k) dX[T + k] += d_final[(int64_t)i * HK + (int64_t)h * K + k];
             for (int64_t u = 0; u < T; ++u) {
                 const double* row = in + (r0 + u) * in_stride;
-                double dbx = 0.0;
-                for (int k = 0; k < K; ++k) {
-                    const int64_t t = u + K - 1 - k;
-                    if (t >= 0 && t < T) dbx += w[(int64_t)h * K + k] * g[t];
-                }
-                d_in[(r0 + u) * 3 * H + h] = dbx * row[2 * H + h];          /* dB  */
-                d_in[(r0 + u) * 3 * H + 2 * H + h] = dbx * row[h];          /* dxv */
+                d_in[(r0 + u) * 3 * H + h] = dX[K + u] * row[2 * H + h];          /* dB  */
+                d_in[(r0 + u) * 3 * H + 2 * H + h] = dX[K + u] * row[h];          /* dxv */
             }
+            if (d_init)
+                for (int k = 0; k < K; ++k) d_init[(int64_t)i * HK + (int64_t)h * K + k] = dX[k];
         }
+        if (dbias) dbias[h] = db;
         free(X);
-        free(g);
+        free(dX);
     }
     return fail ? -1 : 0;
 }

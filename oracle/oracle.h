@@ -45,8 +45,14 @@
  *   - Verify leaves the pool untouched; tape[i][s] is the state after token s
  *     of batch row i; commit with accept length a > 0 installs tape[i][a-1],
  *     a = 0 keeps the old state.
- *   - Backward: no gradient is returned for the initial state, and none flows
- *     in from the returned final state.
+ *   - Conv bias (optional, [H]): added to conv before the C gate.  The MAX
+ *     article's weight-name mapping carries a conv bias and SGLang's excerpt
+ *     passes one to its conv update; the released LFM2 checkpoints are
+ *     bias-free (Liger-Kernel PR, "Gated short convolution").
+ *   - Backward: the gradient of the initial state is returned on request, and a
+ *     gradient arriving at the returned final state may be given (chunked
+ *     training: chunk c+1's initial-state gradient is chunk c's final-state
+ *     gradient).
  *
  * Layouts (all row-major, strides in elements):
  *   in     [rows][in_stride]   columns 0..H-1 = B, H..2H-1 = C, 2H..3H-1 = xv
@@ -57,6 +63,8 @@
  *   dy     [rows][H]
  *   d_in   [rows][3H]          dB | dC | dxv
  *   dW     [H][K]
+ *   bias   [H] (NULL = no bias), dbias [H]
+ *   d_final, d_init  [N][H][K]  (gradients of each sequence's final / initial state)
  *
  * Every function returns 0 on success and -1 if an argument is out of range
  * (the oracle checks what it needs to stay in bounds; it is not a validator).
@@ -84,7 +92,7 @@ int oracle_get_threads(void);
 int oracle_prefill(int H, int K, int64_t total_T,
                    const double* in, int64_t in_stride,
                    const int32_t* cu, int N,
-                   const double* w,
+                   const double* w, const double* bias,
                    double* pool, int64_t num_slots, const int32_t* slot_idx,
                    double* y);
 
@@ -92,7 +100,7 @@ int oracle_prefill(int H, int K, int64_t total_T,
  * state lives in pool[slot_idx[i]] and is advanced in place. */
 int oracle_decode(int H, int K, int N,
                   const double* in, int64_t in_stride,
-                  const double* w,
+                  const double* w, const double* bias,
                   double* pool, int64_t num_slots, const int32_t* slot_idx,
                   double* y);
 
@@ -100,7 +108,7 @@ int oracle_decode(int H, int K, int N,
  * only; tape[i][s] receives the state after token s. */
 int oracle_verify(int H, int K, int N, int L,
                   const double* in, int64_t in_stride,
-                  const double* w,
+                  const double* w, const double* bias,
                   const double* pool, int64_t num_slots, const int32_t* slot_idx,
                   double* tape, double* y);
 
@@ -110,15 +118,17 @@ int oracle_commit(int H, int K, int N, int L,
                   double* pool, int64_t num_slots, const int32_t* slot_idx);
 
 /* Backward of the prefill forward (same sequence and state conventions; pool
- * is read only and may be NULL for zero initial states).  Writes d_in
- * [total_T][3H] = dB | dC | dxv and dW [H][K] (both overwritten). */
+ * is read only and may be NULL for zero initial states).  dy is the gradient
+ * of y; d_final (may be NULL = zero) the gradient of each sequence's returned
+ * final state.  Writes d_in [total_T][3H] = dB | dC | dxv and dW [H][K], and,
+ * when non-NULL, dbias [H] and d_init [N][H][K] (all overwritten). */
 int oracle_backward(int H, int K, int64_t total_T,
                     const double* in, int64_t in_stride,
                     const int32_t* cu, int N,
-                    const double* w,
+                    const double* w, const double* bias,
                     const double* pool, int64_t num_slots, const int32_t* slot_idx,
-                    const double* dy,
-                    double* d_in, double* dW);
+                    const double* dy, const double* d_final,
+                    double* d_in, double* dW, double* dbias, double* d_init);
 
 #ifdef __cplusplus
 }
