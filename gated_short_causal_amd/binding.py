@@ -134,11 +134,20 @@ def lfm2sc_backward_workspace_bytes(dtype, H, K, total_T, num_seqs) -> int:
 
 
 def lfm2sc_backward(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, workspace,
-                    init_state_pool=None, slot_idx=None):
+                    init_state_pool=None, slot_idx=None, bias=None, d_final_state=None, dbias=None,
+                    d_init_state=None):
+    """Backward of lfm2sc_prefill_ragged.  Writes d_in_proj (dB | dC | dxv), dW (fp32), and when given dbias
+    (fp32 [H]) and d_init_state ([N, H, K], I/O dtype).  d_final_state: gradient of the final states [N, H, K]."""
     H, K = _hk(weight)
+    N = cu_seqlens.numel() - 1
     _i32(cu_seqlens, "cu_seqlens"); _i32(slot_idx, "slot_idx")
     if dW.dtype != torch.float32 or not dW.is_contiguous():
         raise TypeError("dW must be a contiguous float32 [H, K] tensor")
+    if dbias is not None and (dbias.dtype != torch.float32 or not dbias.is_contiguous()):
+        raise TypeError("dbias must be a contiguous float32 [H] tensor")
+    for name, t in (("d_final_state", d_final_state), ("d_init_state", d_init_state)):
+        if t is not None and (t.dtype != weight.dtype or not t.is_contiguous() or t.numel() < N * H * K):
+            raise ValueError(f"{name} must be a contiguous [{N}, {H}, {K}] tensor of the I/O dtype")
     num_slots = slot_stride = 0
     if init_state_pool is not None:
         slot_stride = _pool_stride(init_state_pool, H, K)
@@ -146,10 +155,10 @@ def lfm2sc_backward(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, workspace,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lib().lfm2sc_backward(
         _dtype_code(weight), H, K, _ptr(in_proj), _rows(in_proj, "in_proj"), in_proj.shape[0],
-        _ptr(cu_seqlens), cu_seqlens.numel() - 1, _ptr(weight),
+        _ptr(cu_seqlens), N, _ptr(weight), _ptr(bias),
         _ptr(init_state_pool), num_slots, slot_stride, _ptr(slot_idx),
-        _ptr(dy), _rows(dy, "dy"), _ptr(d_in_proj), _rows(d_in_proj, "d_in_proj"), _ptr(dW),
-        _ptr(workspace), ws_bytes, _stream(in_proj.device)))
+        _ptr(dy), _rows(dy, "dy"), _ptr(d_final_state), _ptr(d_in_proj), _rows(d_in_proj, "d_in_proj"), _ptr(dW),
+        _ptr(dbias), _ptr(d_init_state), _ptr(workspace), ws_bytes, _stream(in_proj.device)))
     return d_in_proj, dW
 
 

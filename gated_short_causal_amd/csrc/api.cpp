@@ -56,7 +56,8 @@ int check_common(const char* fn, int dtype, int H, int K, const void* bias) {
     if (H < 8 || H % 8 != 0 || H > kMaxH)
         return fail(LFM2SC_ERR_BAD_SHAPE, "%s: H=%d must be a multiple of 8 in [8, %d]", fn, H, kMaxH);
     if (K < 1 || K > 4) return fail(LFM2SC_ERR_UNSUPPORTED, "%s: K=%d is not in 1..4", fn, K);
-    if (bias != nullptr) return fail(LFM2SC_ERR_UNSUPPORTED, "%s: conv bias is not supported (pass NULL)", fn);
+    if (bias != nullptr && !aligned(bias, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: bias=%p is not 16-byte aligned", fn, bias);
     return LFM2SC_OK;
 }
 
@@ -106,12 +107,12 @@ int device_check(const char* fn, hipStream_t s, const int32_t* slot_idx, int N, 
 
 template <typename E>
 int prefill_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T, const int32_t* cu, int N,
-                 const void* weight, void* pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx,
-                 void* y, int64_t y_stride, hipStream_t s) {
+                 const void* weight, const void* bias, void* pool, int64_t num_slots, int64_t slot_stride,
+                 const int32_t* slot_idx, void* y, int64_t y_stride, hipStream_t s) {
     PrefillArgs<E> a;
     a.in = static_cast<const E*>(in_proj); a.in_stride = in_stride; a.total_T = total_T;
     a.cu = cu; a.N = N;
-    a.w = static_cast<const E*>(weight);
+    a.w = static_cast<const E*>(weight); a.bias = static_cast<const E*>(bias);
     a.pool = static_cast<E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
     a.y = static_cast<E*>(y); a.y_stride = y_stride;
     a.H = H;
@@ -121,19 +122,59 @@ int prefill_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t t
 }
 
 template <typename E>
+int decode_impl(int H, int K, const void* in_proj, int64_t in_stride, int N, const void* weight, const void* bias,
+                void* pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx, void* y, int64_t y_stride,
+                hipStream_t s) {
+    DecodeArgs<E> a;
+    a.in = static_cast<const E*>(in_proj); a.in_stride = in_stride; a.N = N;
+    a.w = static_cast<const E*>(weight); a.bias = static_cast<const E*>(bias);
+    a.pool = static_cast<E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
+    a.y = static_cast<E*>(y); a.y_stride = y_stride;
+    a.H = H;
+    return launched("lfm2sc_decode_step", launch_decode<E>(a, K, s));
+}
+
+template <typename E>
+int verify_impl(int H, int K, const void* in_proj, int64_t in_stride, int N, int L, const void* weight,
+                const void* bias, const void* pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx,
+                void* windows, void* y, int64_t y_stride, hipStream_t s) {
+    VerifyArgs<E> a;
+    a.in = static_cast<const E*>(in_proj); a.in_stride = in_stride; a.N = N; a.L = L;
+    a.w = static_cast<const E*>(weight); a.bias = static_cast<const E*>(bias);
+    a.pool = static_cast<const E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride;
+    a.slot_idx = slot_idx;
+    a.win = static_cast<E*>(windows);
+    a.y = static_cast<E*>(y); a.y_stride = y_stride;
+    a.H = H;
+    return launched("lfm2sc_verify_window", launch_verify<E>(a, K, s));
+}
+
+template <typename E>
+int commit_impl(int H, int K, const void* windows, int N, int L, const int32_t* accept, void* pool, int64_t num_slots,
+                int64_t slot_stride, const int32_t* slot_idx, hipStream_t s) {
+    CommitArgs<E> a;
+    a.win = static_cast<const E*>(windows); a.N = N; a.L = L; a.accept = accept;
+    a.pool = static_cast<E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
+    a.H = H;
+    return launched("lfm2sc_commit_window", launch_commit<E>(a, K, s));
+}
+
+template <typename E>
 int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T, const int32_t* cu, int N,
-                  const void* weight, const void* pool, int64_t num_slots, int64_t slot_stride,
-                  const int32_t* slot_idx, const void* dy, int64_t dy_stride, void* din, int64_t din_stride, float* dW,
-                  void* ws, hipStream_t s) {
+                  const void* weight, const void* bias, const void* pool, int64_t num_slots, int64_t slot_stride,
+                  const int32_t* slot_idx, const void* dy, int64_t dy_stride, const void* dfinal, void* din,
+                  int64_t din_stride, float* dW, float* dbias, void* dinit, void* ws, hipStream_t s) {
     BackwardArgs<E> a;
     a.in = static_cast<const E*>(in_proj); a.in_stride = in_stride; a.total_T = total_T;
     a.cu = cu; a.N = N;
-    a.w = static_cast<const E*>(weight);
+    a.w = static_cast<const E*>(weight); a.bias = static_cast<const E*>(bias);
     a.pool = static_cast<const E*>(pool); a.num_slots = num_slots; a.slot_stride = slot_stride; a.slot_idx = slot_idx;
     a.dy = static_cast<const E*>(dy); a.dy_stride = dy_stride;
+    a.dfinal = static_cast<const E*>(dfinal);
     a.din = static_cast<E*>(din); a.din_stride = din_stride;
     a.partial = ws;
-    a.dW = dW;
+    a.dW = dW; a.dbias = dbias;
+    a.dinit = static_cast<E*>(dinit);
     a.H = H;
     a.sub = 0;
     a.ntiles = 0;
@@ -143,7 +184,7 @@ int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t 
 size_t workspace_bytes(int dtype, int H, int K, int64_t total_T, int N) {
     if (N <= 0 || total_T <= 0) return 0;
     const int64_t nt = backward_partial_rows(dtype == LFM2SC_F32, H, K, total_T, N);
-    const size_t bytes = (size_t)nt * (size_t)H * (size_t)K * (size_t)backward_partial_bytes(dtype == LFM2SC_F32);
+    const size_t bytes = (size_t)nt * (size_t)H * (size_t)(K + 1) * (size_t)backward_partial_bytes(dtype == LFM2SC_F32);
     return (bytes + 255) / 256 * 256;
 }
 
@@ -191,10 +232,10 @@ int lfm2sc_prefill_ragged(int dtype, int H, int K, const void* in_proj, int64_t 
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, state_pool ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens, total_T, nullptr, 0));
     if (dtype == LFM2SC_BF16)
-        return prefill_impl<uint16_t>(H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs, weight, state_pool,
-                                      num_slots, slot_stride, slot_idx, y, y_stride, s);
-    return prefill_impl<float>(H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs, weight, state_pool, num_slots,
-                               slot_stride, slot_idx, y, y_stride, s);
+        return prefill_impl<uint16_t>(H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs, weight, bias,
+                                      state_pool, num_slots, slot_stride, slot_idx, y, y_stride, s);
+    return prefill_impl<float>(H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs, weight, bias, state_pool,
+                               num_slots, slot_stride, slot_idx, y, y_stride, s);
 }
 
 int lfm2sc_decode_step(int dtype, int H, int K, const void* in_proj, int64_t in_stride, int num_seqs,
@@ -212,16 +253,11 @@ int lfm2sc_decode_step(int dtype, int H, int K, const void* in_proj, int64_t in_
     TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, slot_idx, num_seqs, num_slots, nullptr, 0, nullptr, 0));
-    if (dtype == LFM2SC_BF16) {
-        DecodeArgs<uint16_t> a{static_cast<const uint16_t*>(in_proj), in_stride, num_seqs,
-                               static_cast<const uint16_t*>(weight), static_cast<uint16_t*>(state_pool), num_slots,
-                               slot_stride, slot_idx, static_cast<uint16_t*>(y), y_stride, H};
-        return launched(fn, launch_decode<uint16_t>(a, K, s));
-    }
-    DecodeArgs<float> a{static_cast<const float*>(in_proj), in_stride, num_seqs, static_cast<const float*>(weight),
-                        static_cast<float*>(state_pool), num_slots, slot_stride, slot_idx, static_cast<float*>(y),
-                        y_stride, H};
-    return launched(fn, launch_decode<float>(a, K, s));
+    if (dtype == LFM2SC_BF16)
+        return decode_impl<uint16_t>(H, K, in_proj, in_stride, num_seqs, weight, bias, state_pool, num_slots,
+                                     slot_stride, slot_idx, y, y_stride, s);
+    return decode_impl<float>(H, K, in_proj, in_stride, num_seqs, weight, bias, state_pool, num_slots, slot_stride,
+                              slot_idx, y, y_stride, s);
 }
 
 int lfm2sc_verify_window(int dtype, int H, int K, const void* in_proj, int64_t in_stride, int num_seqs, int L,
@@ -244,17 +280,11 @@ int lfm2sc_verify_window(int dtype, int H, int K, const void* in_proj, int64_t i
     TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, slot_idx, num_seqs, num_slots, nullptr, 0, nullptr, 0));
-    if (dtype == LFM2SC_BF16) {
-        VerifyArgs<uint16_t> a{static_cast<const uint16_t*>(in_proj), in_stride, num_seqs, L,
-                               static_cast<const uint16_t*>(weight), static_cast<const uint16_t*>(state_pool),
-                               num_slots, slot_stride, slot_idx, static_cast<uint16_t*>(windows),
-                               static_cast<uint16_t*>(y), y_stride, H};
-        return launched(fn, launch_verify<uint16_t>(a, K, s));
-    }
-    VerifyArgs<float> a{static_cast<const float*>(in_proj), in_stride, num_seqs, L, static_cast<const float*>(weight),
-                        static_cast<const float*>(state_pool), num_slots, slot_stride, slot_idx,
-                        static_cast<float*>(windows), static_cast<float*>(y), y_stride, H};
-    return launched(fn, launch_verify<float>(a, K, s));
+    if (dtype == LFM2SC_BF16)
+        return verify_impl<uint16_t>(H, K, in_proj, in_stride, num_seqs, L, weight, bias, state_pool, num_slots,
+                                     slot_stride, slot_idx, windows, y, y_stride, s);
+    return verify_impl<float>(H, K, in_proj, in_stride, num_seqs, L, weight, bias, state_pool, num_slots, slot_stride,
+                              slot_idx, windows, y, y_stride, s);
 }
 
 int lfm2sc_commit_window(int dtype, int H, int K, const void* windows, int num_seqs, int L, const int32_t* accept_len,
@@ -269,14 +299,10 @@ int lfm2sc_commit_window(int dtype, int H, int K, const void* windows, int num_s
     TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, slot_idx, num_seqs, num_slots, nullptr, 0, accept_len, L));
-    if (dtype == LFM2SC_BF16) {
-        CommitArgs<uint16_t> a{static_cast<const uint16_t*>(windows), num_seqs, L, accept_len,
-                               static_cast<uint16_t*>(state_pool), num_slots, slot_stride, slot_idx, H};
-        return launched(fn, launch_commit<uint16_t>(a, K, s));
-    }
-    CommitArgs<float> a{static_cast<const float*>(windows), num_seqs, L, accept_len, static_cast<float*>(state_pool),
-                        num_slots, slot_stride, slot_idx, H};
-    return launched(fn, launch_commit<float>(a, K, s));
+    if (dtype == LFM2SC_BF16)
+        return commit_impl<uint16_t>(H, K, windows, num_seqs, L, accept_len, state_pool, num_slots, slot_stride,
+                                     slot_idx, s);
+    return commit_impl<float>(H, K, windows, num_seqs, L, accept_len, state_pool, num_slots, slot_stride, slot_idx, s);
 }
 
 size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T, int num_seqs) {
@@ -287,12 +313,13 @@ size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T,
 }
 
 int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T,
-                    const int32_t* cu_seqlens, int num_seqs, const void* weight, const void* init_state_pool,
-                    int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx, const void* dy,
-                    int64_t dy_stride, void* d_in_proj, int64_t din_stride, float* dW, void* workspace,
-                    size_t workspace_bytes_, void* stream) {
+                    const int32_t* cu_seqlens, int num_seqs, const void* weight, const void* bias,
+                    const void* init_state_pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx,
+                    const void* dy, int64_t dy_stride, const void* d_final_state, void* d_in_proj, int64_t din_stride,
+                    float* dW, float* dbias, void* d_init_state, void* workspace, size_t workspace_bytes_,
+                    void* stream) {
     const char* fn = "lfm2sc_backward";
-    TRY(check_common(fn, dtype, H, K, nullptr));
+    TRY(check_common(fn, dtype, H, K, bias));
     if (num_seqs < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d is negative", fn, num_seqs);
     if (total_T < 0 || total_T >= kMaxRows)
         return fail(LFM2SC_ERR_BAD_SHAPE, "%s: total_T=%lld outside [0, 2^31)", fn, (long long)total_T);
@@ -300,10 +327,15 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
     TRY(check_stride(fn, "dy_stride", dy_stride, H));
     TRY(check_stride(fn, "din_stride", din_stride, 3 * (int64_t)H));
     TRY(check_ptr(fn, "dW", dW, 4));
+    if (dbias != nullptr && !aligned(dbias, 4)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: dbias is not 4-byte aligned", fn);
+    if (d_final_state != nullptr && !aligned(d_final_state, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_final_state is not 16-byte aligned", fn);
+    if (d_init_state != nullptr && !aligned(d_init_state, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_init_state is not 16-byte aligned", fn);
     const bool work = num_seqs > 0 && total_T > 0;
+    if (num_seqs > 0) TRY(check_ptr(fn, "cu_seqlens", cu_seqlens, 4));
     if (work) {
         TRY(check_ptr(fn, "in_proj", in_proj, 16));
-        TRY(check_ptr(fn, "cu_seqlens", cu_seqlens, 4));
         TRY(check_ptr(fn, "weight", weight, 16));
         TRY(check_ptr(fn, "dy", dy, 16));
         TRY(check_ptr(fn, "d_in_proj", d_in_proj, 16));
@@ -318,18 +350,19 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
         if (!aligned(workspace, 16)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: workspace is not 16-byte aligned", fn);
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (work)
-        TRY(device_check(fn, s, init_state_pool ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens, total_T,
-                         nullptr, 0));
-    // With no token the launch still runs the dW finish over zero windows, which writes dW = 0.
+    if (num_seqs > 0)
+        TRY(device_check(fn, s, (work && init_state_pool) ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens,
+                         total_T, nullptr, 0));
+    // With no token the launch still runs the reduction over zero windows (dW = 0, dbias = 0) and, when asked,
+    // writes d_init_state = d_final_state (or 0) for every (empty) sequence.
     const int64_t T_eff = work ? total_T : 0;
-    const int N_eff = work ? num_seqs : 0;
     if (dtype == LFM2SC_BF16)
-        return backward_impl<uint16_t>(H, K, in_proj, in_stride, T_eff, cu_seqlens, N_eff, weight, init_state_pool,
-                                       num_slots, slot_stride, slot_idx, dy, dy_stride, d_in_proj, din_stride, dW,
-                                       workspace, s);
-    return backward_impl<float>(H, K, in_proj, in_stride, T_eff, cu_seqlens, N_eff, weight, init_state_pool, num_slots,
-                                slot_stride, slot_idx, dy, dy_stride, d_in_proj, din_stride, dW, workspace, s);
+        return backward_impl<uint16_t>(H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias,
+                                       init_state_pool, num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state,
+                                       d_in_proj, din_stride, dW, dbias, d_init_state, workspace, s);
+    return backward_impl<float>(H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias, init_state_pool,
+                                num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state, d_in_proj, din_stride,
+                                dW, dbias, d_init_state, workspace, s);
 }
 
 }  // extern "C"

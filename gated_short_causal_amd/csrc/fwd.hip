@@ -18,14 +18,14 @@ namespace lfm2sc {
 // of the padded history X = [state | bx...] for the current token t.
 template <typename E, int K>
 __device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, const Raw8<E>& rx,
-                                          const float (&wf)[kChPerLane][K],
+                                          const float (&wf)[kChPerLane][K], const float (&bv)[kChPerLane],
                                           float (&hist)[kChPerLane][K > 1 ? K - 1 : 1], rsrc_t yrow, uint32_t yoff) {
     float b[8], c[8], x[8], yv[8];
     to_f32(rb, b); to_f32(rc, c); to_f32(rx, x);
 #pragma unroll
     for (int ch = 0; ch < 8; ++ch) {
         const float bx = b[ch] * x[ch];
-        float conv = wf[ch][K - 1] * bx;
+        float conv = fmaf(wf[ch][K - 1], bx, bv[ch]);
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[ch][k], hist[ch][k], conv);
         yv[ch] = c[ch] * conv;
@@ -77,6 +77,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
 
     float wf[kChPerLane][K];
     load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float bv[kChPerLane] = {};
+    if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
 
     E* slotp = nullptr;
     if (owner && a.pool != nullptr) {
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
     auto use_batch = [&](const Raw8<E> (&rb)[U], const Raw8<E> (&rc)[U], const Raw8<E> (&rx)[U], int64_t t0) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, row_rsrc(y_rows + (t0 + u) * a.y_stride, y_row_bytes), offB);
+            fwd_token<E, K>(rb[u], rc[u], rx[u], wf, bv, hist, row_rsrc(y_rows + (t0 + u) * a.y_stride, y_row_bytes), offB);
     };
     for (; t + U <= hi; t += U) {
         Raw8<E> rb[U], rc[U], rx[U];
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if (u < n)
-                fwd_token<E, K>(rb[u], rc[u], rx[u], wf, hist, row_rsrc(y_rows + (t + u) * a.y_stride, y_row_bytes),
+                fwd_token<E, K>(rb[u], rc[u], rx[u], wf, bv, hist, row_rsrc(y_rows + (t + u) * a.y_stride, y_row_bytes),
                                 offB);
     }
 
@@ -220,6 +222,8 @@ __global__ __launch_bounds__(kSmallBlock) void decode_kernel(const DecodeArgs<E>
     const Raw8<E> rb = ld8<E>(row), rc = ld8<E>(row + H), rx = ld8<E>(row + 2 * H);
     float wf[kChPerLane][K];
     load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float bv[kChPerLane] = {};
+    if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
     E* sp = ok ? a.pool + slot * a.slot_stride + (int64_t)ch0 * K : nullptr;
     float s[kChPerLane][K];
     if (ok) {
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(kSmallBlock) void decode_kernel(const DecodeArgs<E>
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
         s[c][K - 1] = b[c] * x[c];
-        float conv = wf[c][K - 1] * s[c][K - 1];
+        float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
 #pragma unroll
         for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
         yv[c] = c8[c] * conv;
@@ -259,6 +263,8 @@ __global__ __launch_bounds__(kSmallBlock) void verify_kernel(const VerifyArgs<E>
     const int64_t slot = a.slot_idx[i];
     float wf[kChPerLane][K];
     load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float bv[kChPerLane] = {};
+    if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
     float s[kChPerLane][K];
     if (slot_ok(slot, a.num_slots)) {
         load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, s);
@@ -280,7 +286,7 @@ __global__ __launch_bounds__(kSmallBlock) void verify_kernel(const VerifyArgs<E>
 #pragma unroll
             for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
             s[c][K - 1] = b[c] * x[c];
-            float conv = wf[c][K - 1] * s[c][K - 1];
+            float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
 #pragma unroll
             for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
             yv[c] = c8[c] * conv;

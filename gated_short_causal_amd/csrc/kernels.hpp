@@ -12,7 +12,7 @@ template <typename E>
 struct PrefillArgs {
     const E* in; int64_t in_stride; int64_t total_T;
     const int32_t* cu; int N;
-    const E* w;
+    const E* w; const E* bias;
     E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     E* y; int64_t y_stride;
     int H;
@@ -23,7 +23,7 @@ struct PrefillArgs {
 template <typename E>
 struct DecodeArgs {
     const E* in; int64_t in_stride; int N;
-    const E* w;
+    const E* w; const E* bias;
     E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     E* y; int64_t y_stride;
     int H;
@@ -32,7 +32,7 @@ struct DecodeArgs {
 template <typename E>
 struct VerifyArgs {
     const E* in; int64_t in_stride; int N; int L;
-    const E* w;
+    const E* w; const E* bias;
     const E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     E* win;
     E* y; int64_t y_stride;
@@ -50,20 +50,23 @@ template <typename E>
 struct BackwardArgs {
     const E* in; int64_t in_stride; int64_t total_T;
     const int32_t* cu; int N;
-    const E* w;
+    const E* w; const E* bias;
     const E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
     const E* dy; int64_t dy_stride;
+    const E* dfinal;  // [N][H][K] gradient of the final states, or nullptr
     E* din; int64_t din_stride;
-    void* partial;    // [ntiles][H*K] per-window dW sums (fp32 for bf16 I/O, fp64 for fp32 I/O)
+    void* partial;    // [ntiles][H][K+1] per-window dW/dbias sums (fp32 for bf16 I/O, fp64 for fp32 I/O)
     float* dW;        // [H][K]
+    float* dbias;     // [H] or nullptr
+    E* dinit;         // [N][H][K] gradient of the initial states, or nullptr
     int H;
     int sub;
     int ntiles;
 };
 
-// Rows of dW partials (one per workgroup window) a backward launch of these
-// sizes writes to its workspace, and the bytes of one partial element; the
-// launcher and the workspace-size query share this.
+// Rows of dW/dbias partials (one per workgroup window, H*(K+1) elements each)
+// a backward launch of these sizes writes to its workspace, and the bytes of
+// one partial element; the launcher and the workspace-size query share this.
 int64_t backward_partial_rows(int dtype_is_f32, int H, int K, int64_t total_T, int N);
 int backward_partial_bytes(int dtype_is_f32);
 // Upper bound on ragged windows for any tiling (host-side size checks).

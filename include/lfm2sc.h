@@ -36,10 +36,12 @@
  *  - Requirements checked on the host: 8 <= H, H % 8 == 0; 1 <= K <= 4; every
  *    device base pointer 16-byte aligned (dW: 4-byte); every stride a multiple
  *    of 8 elements; in_stride >= 3H, y_stride >= H, dy_stride >= H,
- *    din_stride >= 3H, slot_stride >= H*K.  A non-NULL bias is rejected with
- *    LFM2SC_ERR_UNSUPPORTED in this version (the released LFM2 checkpoints are
- *    bias-free, as the Liger-Kernel LFM2 PR notes under "Gated short
- *    convolution").
+ *    din_stride >= 3H, slot_stride >= H*K.
+ *  - bias: optional conv bias [H] (same dtype as the weight, 16-byte aligned),
+ *    added to conv before the C gate; NULL = none.  The MAX article's
+ *    weight-name mapping carries a conv bias and SGLang's verify excerpt passes
+ *    one to its conv update; the released LFM2 checkpoints are bias-free
+ *    (Liger-Kernel LFM2 PR, "Gated short convolution").
  *  - Device-side data (slot indices, row offsets, accept lengths) cannot be
  *    checked on the host without a synchronisation.  Kernels never access
  *    memory outside the buffers described by the size arguments: a slot index
@@ -63,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LFM2SC_ABI_VERSION 1
+#define LFM2SC_ABI_VERSION 2
 
 enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
 
@@ -89,7 +91,7 @@ enum lfm2sc_status {
  * in_proj    [total_T][in_stride]  packed rows of all sequences (B | C | xv).
  * cu_seqlens [num_seqs+1] int32    sequence i owns rows [cu[i], cu[i+1]);
  *                                  non-decreasing; cu[N] <= total_T.
- * weight     [H][K].  bias: must be NULL.
+ * weight     [H][K].  bias: [H] or NULL.
  * state_pool [num_slots][slot_stride] or NULL.  NULL: every sequence starts
  *            from a zero state and no state is written (training forward).
  *            Otherwise sequence i starts from pool[slot_idx[i]] and, in
@@ -173,7 +175,7 @@ int lfm2sc_commit_window(int dtype, int H, int K,
 
 /*
  * Bytes of device workspace lfm2sc_backward needs for these sizes (it holds
- * per-tile fp32 partial sums of dW).  Returns 0 for invalid sizes.
+ * per-window partial sums of dW and dbias).  Returns 0 for invalid sizes.
  */
 size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T, int num_seqs);
 
@@ -183,31 +185,41 @@ size_t lfm2sc_backward_workspace_bytes(int dtype, int H, int K, int64_t total_T,
  * Passage: Liger-Kernel PR 1317 ("Add LFM2, LFM2-MoE, and LFM2-VL support"),
  * "Kernel changes / Gated short convolution": gradients through both gates and
  * the conv input, and a weight gradient that gathers all K taps of a channel.
- * The formulas are the derivatives of the forward: with g = dy*C,
- *   dC = dy * conv;  dbx[u] = sum_k w[k] g[u+K-1-k] (inside the sequence);
- *   dB = dbx * xv;   dxv = dbx * B;   dW[h][k] = sum over tokens of g * (the
- *   state entry k that multiplied w[h][k]).
+ * The formulas are the chain rule on the forward: with X = [initial state |
+ * bx of the sequence], conv[t] = bias + sum_k w[k] X[t+1+k], g = dy*C,
+ *   dC = dy * conv;  dX[j] = sum over (t, k) with t+1+k = j of w[k] g[t]
+ *   (+ the final-state gradient on the last K entries of X);
+ *   dB = dX[K+u] * xv;  dxv = dX[K+u] * B;  d_init = dX[0..K-1];
+ *   dW[h][k] = sum over tokens of g * X[t+1+k];  dbias[h] = sum over tokens of g.
  *
- * in_proj, cu_seqlens, weight: as for the forward call.
+ * in_proj, cu_seqlens, weight, bias: as for the forward call (bias may be NULL).
  * init_state_pool / num_slots / slot_stride / slot_idx: the initial states the
- *            forward started from (read only); NULL pool = zero states.  No
- *            gradient is returned for them.
+ *            forward started from (read only); NULL pool = zero states.
  * dy         [total_T][dy_stride].
+ * d_final_state [num_seqs][H][K] dense, or NULL (= zero): gradient arriving at
+ *            each sequence's returned final state (chunked training: the
+ *            d_init_state of the next chunk of the same sequences).
  * d_in_proj  [total_T][din_stride]  columns dB | dC | dxv (overwritten).
- * dW         [H][K] fp32 (overwritten; reduced over all sequences and tokens
- *            in a fixed order, so results are bitwise reproducible).
+ * dW         [H][K] fp32 (overwritten); dbias [H] fp32 or NULL (overwritten).
+ *            Both are reduced over all sequences and tokens in a fixed order,
+ *            so results are bitwise reproducible.
+ * d_init_state [num_seqs][H][K] dense, I/O dtype, or NULL: gradient of each
+ *            sequence's initial state (overwritten; entry 0 of a sequence with
+ *            at least one token is always 0, that entry being shifted out).
  * workspace  device buffer of at least lfm2sc_backward_workspace_bytes(...)
  *            bytes, 16-byte aligned; contents on entry are ignored.
  */
 int lfm2sc_backward(int dtype, int H, int K,
                     const void* in_proj, int64_t in_stride, int64_t total_T,
                     const int32_t* cu_seqlens, int num_seqs,
-                    const void* weight,
+                    const void* weight, const void* bias,
                     const void* init_state_pool, int64_t num_slots, int64_t slot_stride,
                     const int32_t* slot_idx,
                     const void* dy, int64_t dy_stride,
+                    const void* d_final_state,
                     void* d_in_proj, int64_t din_stride,
-                    float* dW,
+                    float* dW, float* dbias,
+                    void* d_init_state,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static text for a status code (never NULL). */

@@ -63,7 +63,7 @@ def _prefill(L, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=2), UNSUP), (dict(H=0), SHAPE), (dict(H=12), SHAPE), (dict(H=4), SHAPE),
-    (dict(K=0), UNSUP), (dict(K=5), UNSUP), (dict(bias=P), UNSUP),
+    (dict(K=0), UNSUP), (dict(K=5), UNSUP), (dict(bias=MIS), ALIGN),
     (dict(N=-1), SHAPE), (dict(total_T=-1), SHAPE), (dict(total_T=1 << 31), SHAPE),
     (dict(in_stride=700), SHAPE), (dict(in_stride=772), ALIGN), (dict(y_stride=100), SHAPE), (dict(y_stride=260), ALIGN),
     (dict(in_proj=None), NULLP), (dict(cu=None), NULLP), (dict(w=None), NULLP), (dict(y=None), NULLP),
@@ -98,7 +98,7 @@ def _decode(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(pool=None), NULLP), (dict(slot_idx=None), NULLP), (dict(y=None), NULLP), (dict(in_proj=None), NULLP),
     (dict(N=-3), SHAPE), (dict(num_slots=0), SHAPE), (dict(slot_stride=6136), SHAPE), (dict(dtype=7), UNSUP),
-    (dict(bias=P), UNSUP), (dict(in_stride=6148), ALIGN), (dict(pool=MIS), ALIGN), (dict(slot_idx=P + 1), ALIGN),
+    (dict(bias=P + 8), ALIGN), (dict(in_stride=6148), ALIGN), (dict(pool=MIS), ALIGN), (dict(slot_idx=P + 1), ALIGN),
 ])
 def test_decode_rejects(L, kw, code):
     assert _decode(L, **kw) == code
@@ -143,13 +143,14 @@ def test_commit_no_work(L):
 
 
 def _bwd(L, **kw):
-    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, total_T=4096, cu=P, N=1, w=P, pool=None, num_slots=0,
-             slot_stride=0, slot_idx=None, dy=P, dy_stride=2048, din=P, din_stride=6144, dW=P, ws=P, ws_bytes=1 << 30,
-             stream=None)
+    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, total_T=4096, cu=P, N=1, w=P, bias=None, pool=None,
+             num_slots=0, slot_stride=0, slot_idx=None, dy=P, dy_stride=2048, dfinal=None, din=P, din_stride=6144,
+             dW=P, dbias=None, dinit=None, ws=P, ws_bytes=1 << 30, stream=None)
     a.update(kw)
     return L.lfm2sc_backward(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["total_T"], a["cu"], a["N"],
-                             a["w"], a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"], a["dy"],
-                             a["dy_stride"], a["din"], a["din_stride"], a["dW"], a["ws"], a["ws_bytes"], a["stream"])
+                             a["w"], a["bias"], a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"], a["dy"],
+                             a["dy_stride"], a["dfinal"], a["din"], a["din_stride"], a["dW"], a["dbias"], a["dinit"],
+                             a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -157,6 +158,8 @@ def _bwd(L, **kw):
     (dict(ws=None), WS), (dict(ws_bytes=16), WS), (dict(ws=P + 8), ALIGN), (dict(din_stride=6000), SHAPE),
     (dict(dy_stride=2044), SHAPE), (dict(dy_stride=2052), ALIGN), (dict(cu=None), NULLP),
     (dict(pool=P, num_slots=2, slot_stride=6144, slot_idx=None), NULLP), (dict(K=0), UNSUP),
+    (dict(bias=P + 4, dW=None), ALIGN), (dict(dbias=P + 2), ALIGN), (dict(dfinal=P + 8), ALIGN),
+    (dict(dinit=P + 8), ALIGN),
 ])
 def test_backward_rejects(L, kw, code):
     assert _bwd(L, **kw) == code

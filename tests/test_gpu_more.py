@@ -253,3 +253,126 @@ def test_check_mode_reports_bad_device_data():
     assert r.returncode == 0, r.stderr[-2000:]
     line = [l for l in r.stdout.splitlines() if l.startswith("STATUS")][0]
     assert line == "STATUS [0, 6, 6, 6, 6]", line
+
+
+# ------------------------------------------------------------------ conv bias and state gradients (ABI v2)
+
+def _bias(H, dtype, seed):
+    return (torch.randn(H, generator=torch.Generator().manual_seed(seed)) * 0.5).to(dtype)
+
+
+@pytest.mark.parametrize("K,dtype", [(3, torch.bfloat16), (4, torch.float32), (1, torch.bfloat16)])
+def test_bias_all_entry_points(K, dtype):
+    _say(f"case: conv bias K={K} {dtype}")
+    H = 520
+    lens = [9, 1, 0, 40, 2]
+    c = wl.random_case(90 + K, lens, H=H, K=K, dtype=dtype, slots=8, with_dy=True)
+    b = _bias(H, dtype, 91)
+    g = c.to(DEV)
+    bd = b.to(DEV)
+    pool0 = g.pool.clone()
+    T, N = sum(lens), len(lens)
+    y = _nan((T, H), dtype)
+    lfm2sc_prefill_ragged(g.inp, g.cu, g.w, y, g.pool, g.slot_idx, bias=bd)
+    torch.cuda.synchronize()
+    y_ref, p_ref = oracle.prefill(c.inp, c.cu, c.w, c.pool, c.slot_idx, bias=b)
+    assert_close(y, y_ref, dtype, "prefill y with bias")
+    assert_bits(g.pool, rounded(p_ref, dtype), "prefill states with bias")
+    # decode and verify on the original pool
+    g.pool.copy_(pool0)
+    yd = _nan((N, H), dtype)
+    rows = torch.arange(N)
+    lfm2sc_decode_step(g.inp[rows.to(DEV)].contiguous(), g.w, g.pool, g.slot_idx, yd, bias=bd)
+    torch.cuda.synchronize()
+    yd_ref, pd_ref = oracle.decode(c.inp[rows], c.w, c.pool, c.slot_idx, bias=b)
+    assert_close(yd, yd_ref, dtype, "decode y with bias")
+    assert_bits(g.pool, rounded(pd_ref, dtype), "decode states with bias")
+    g.pool.copy_(pool0)
+    L = 2
+    vin = g.inp[:N * L].contiguous()
+    yv = _nan((N * L, H), dtype)
+    win = _nan((N, L, H, K), dtype)
+    lfm2sc_verify_window(vin, g.w, g.pool, g.slot_idx, L, win, yv, bias=bd)
+    torch.cuda.synchronize()
+    yv_ref, tape_ref = oracle.verify(c.inp[:N * L], c.w, c.pool, c.slot_idx, L, bias=b)
+    assert_close(yv, yv_ref, dtype, "verify y with bias")
+    assert_bits(win, rounded(tape_ref, dtype), "verify tape with bias")
+    # backward with bias: dC includes it, dbias = sum of g
+    d_in = _nan((T, 3 * H), dtype)
+    dW = _nan((H, K), torch.float32)
+    db = _nan((H,), torch.float32)
+    ws = torch.empty(lfm2sc_backward_workspace_bytes(dtype, H, K, T, N), dtype=torch.uint8, device=DEV)
+    lfm2sc_backward(g.inp, g.cu, g.w, g.dy, d_in, dW, ws, pool0, g.slot_idx, bias=bd, dbias=db)
+    torch.cuda.synchronize()
+    d_ref, dW_ref, db_ref, _ = oracle.backward(c.inp, c.cu, c.w, c.dy, c.pool, c.slot_idx, bias=b, full=True)
+    assert_close(d_in, d_ref, dtype, "d_in with bias")
+    assert_close(dW, dW_ref, dtype, "dW with bias")
+    assert_close(db, db_ref, dtype, "dbias")
+
+
+@pytest.mark.parametrize("K,dtype,lens", [
+    (3, torch.bfloat16, [50, 1, 0, 2, 300, 3]),
+    (4, torch.float32, [7, 0, 3, 129, 1]),
+    (2, torch.bfloat16, [1, 64, 0]),
+    (1, torch.float32, [5, 0, 2]),
+])
+def test_state_gradients(K, dtype, lens):
+    _say(f"case: state gradients K={K} {dtype} lens={lens}")
+    H = 264
+    c = wl.random_case(95 + K, lens, H=H, K=K, dtype=dtype, slots=len(lens) + 3, with_dy=True)
+    T, N = sum(lens), len(lens)
+    dF = torch.randn(N, H, K, generator=torch.Generator().manual_seed(96)).to(dtype)
+    g = c.to(DEV)
+    d_in = _nan((T, 3 * H), dtype)
+    dW = _nan((H, K), torch.float32)
+    db = _nan((H,), torch.float32)
+    dinit = _nan((N, H, K), dtype)
+    ws = torch.empty(max(16, lfm2sc_backward_workspace_bytes(dtype, H, K, T, N)), dtype=torch.uint8, device=DEV)
+    lfm2sc_backward(g.inp, g.cu, g.w, g.dy, d_in, dW, ws, g.pool, g.slot_idx, d_final_state=dF.to(DEV), dbias=db,
+                    d_init_state=dinit)
+    torch.cuda.synchronize()
+    d_ref, dW_ref, db_ref, di_ref = oracle.backward(c.inp, c.cu, c.w, c.dy, c.pool, c.slot_idx, d_final=dF, full=True)
+    assert_close(d_in, d_ref, dtype, "d_in with d_final")
+    assert_close(dW, dW_ref, dtype, "dW")
+    assert_close(db, db_ref, dtype, "dbias")
+    assert_close(dinit, di_ref, dtype, "d_init")
+    # without d_final: the initial-state gradient comes from the conv terms alone
+    lfm2sc_backward(g.inp, g.cu, g.w, g.dy, d_in, dW, ws, g.pool, g.slot_idx, d_init_state=dinit)
+    torch.cuda.synchronize()
+    d_ref, _, _, di_ref = oracle.backward(c.inp, c.cu, c.w, c.dy, c.pool, c.slot_idx, full=True)
+    assert_close(d_in, d_ref, dtype, "d_in without d_final")
+    assert_close(dinit, di_ref, dtype, "d_init without d_final")
+
+
+def test_chunked_training_on_gpu():
+    """A long sequence trained in two chunks on the GPU (forward chunk 1, forward chunk 2 from its state,
+    backward chunk 2, backward chunk 1 with chunk 2's d_init as d_final) against the oracle's backward of the
+    whole sequence."""
+    _say("case: chunked training on the GPU")
+    H, K, T, cut = 1024, 3, 3000, 1234
+    c = wl.random_case(97, [T], H=H, K=K, dtype=torch.bfloat16, slots=2, with_dy=True)
+    g = c.to(DEV)
+    pool0 = g.pool.clone()
+    cu1 = torch.tensor([0, cut], dtype=torch.int32, device=DEV)
+    cu2 = torch.tensor([0, T - cut], dtype=torch.int32, device=DEV)
+    in1, in2 = g.inp[:cut].contiguous(), g.inp[cut:].contiguous()
+    y1 = _nan((cut, H), c.dtype)
+    y2 = _nan((T - cut, H), c.dtype)
+    lfm2sc_prefill_ragged(in1, cu1, g.w, y1, g.pool, g.slot_idx)
+    pool_mid = g.pool.clone()
+    lfm2sc_prefill_ragged(in2, cu2, g.w, y2, g.pool, g.slot_idx)
+    ws = torch.empty(lfm2sc_backward_workspace_bytes(c.dtype, H, K, T, 1), dtype=torch.uint8, device=DEV)
+    d2 = _nan((T - cut, 3 * H), c.dtype)
+    dW2 = _nan((H, K), torch.float32)
+    dS_mid = _nan((1, H, K), c.dtype)
+    lfm2sc_backward(in2, cu2, g.w, g.dy[cut:].contiguous(), d2, dW2, ws, pool_mid, g.slot_idx, d_init_state=dS_mid)
+    d1 = _nan((cut, 3 * H), c.dtype)
+    dW1 = _nan((H, K), torch.float32)
+    dS0 = _nan((1, H, K), c.dtype)
+    lfm2sc_backward(in1, cu1, g.w, g.dy[:cut].contiguous(), d1, dW1, ws, pool0, g.slot_idx, d_final_state=dS_mid,
+                    d_init_state=dS0)
+    torch.cuda.synchronize()
+    d_ref, dW_ref, _, di_ref = oracle.backward(c.inp, c.cu, c.w, c.dy, c.pool, c.slot_idx, full=True)
+    assert_close(torch.cat([d1, d2]), d_ref, c.dtype, "chunked d_in")
+    assert_close(dW1 + dW2, dW_ref, c.dtype, "chunked dW")
+    assert_close(dS0, di_ref, c.dtype, "chunked d_init")
