@@ -27,6 +27,8 @@
 // in a fixed order, one partial row per workgroup window goes to the
 // workspace, and a second small kernel sums the rows in a fixed order.  No
 // atomics, so every output is bitwise reproducible.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -73,7 +75,9 @@ struct FinalGrad {
 };
 
 // Emit dB, dxv of token u from the K g values in st.gw (gw[a] = g[u+K-1-a]).
-template <typename E, int K>
+// DF = false is the batched loop's form: it never meets the last K tokens of
+// a sequence while a final-state gradient is given.
+template <typename E, int K, bool DF>
 __device__ __forceinline__ void emit_dbx(BwdState<E, K>& st, const float* bu, const float* xu, int64_t u,
                                          const FinalGrad<E>& fg, rsrc_t du_row, const DinOffsets& o) {
     using A = typename BwdState<E, K>::A;
@@ -85,7 +89,7 @@ __device__ __forceinline__ void emit_dbx(BwdState<E, K>& st, const float* bu, co
         for (int k = 1; k < K; ++k) v = fma_a<A>(st.wf[ch][k], st.gw[ch][k], v);
         dbx[ch] = v;
     }
-    if (fg.blk != nullptr && u >= fg.u_first) {
+    if (DF && fg.blk != nullptr && u >= fg.u_first) {
         // token u is among the last K: its bx is entry K+u-T of the final state
         float df[kChPerLane][K];
         load_block<E, K>(fg.blk, df);
@@ -108,7 +112,7 @@ __device__ __forceinline__ void emit_dbx(BwdState<E, K>& st, const float* bu, co
 
 // Row r of the window: all four operands loaded.  Emits dC[r] and, if `emit`,
 // dB/dxv of u = r-K+1.
-template <typename E, int K>
+template <typename E, int K, bool DF>
 __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, const Raw8<E>& rb, const Raw8<E>& rc,
                                         const Raw8<E>& rx, rsrc_t dc_row, bool emit, int64_t u, const FinalGrad<E>& fg,
                                         rsrc_t du_row, const DinOffsets& o) {
@@ -141,7 +145,7 @@ __device__ __forceinline__ void bwd_row(BwdState<E, K>& st, const Raw8<E>& rdy, 
         float bu[8], xu[8];
         if constexpr (K > 1) { to_f32(st.fb[K - 2], bu); to_f32(st.fx[K - 2], xu); }
         else { to_f32(rb, bu); to_f32(rx, xu); }
-        emit_dbx<E, K>(st, bu, xu, u, fg, du_row, o);
+        emit_dbx<E, K, DF>(st, bu, xu, u, fg, du_row, o);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -165,7 +169,7 @@ __device__ __forceinline__ void bwd_tail_row(BwdState<E, K>& st, const typename 
         float bu[8], xu[8];
         to_f32(st.fb[K - 2 >= 0 ? K - 2 : 0], bu);
         to_f32(st.fx[K - 2 >= 0 ? K - 2 : 0], xu);
-        emit_dbx<E, K>(st, bu, xu, u, fg, du_row, o);
+        emit_dbx<E, K, true>(st, bu, xu, u, fg, du_row, o);
     }
     if constexpr (K > 1) {
 #pragma unroll
@@ -270,31 +274,38 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t rr = t0 + u;
-            bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], din_row(rr), true, rr - (K - 1), fg, din_row(rr - (K - 1)),
-                          o);
+            bwd_row<E, K, false>(st, rdy[u], rb[u], rc[u], rx[u], din_row(rr), true, rr - (K - 1), fg,
+                                 din_row(rr - (K - 1)), o);
         }
     };
+    // One row on its own (u = r-K+1 emitted when inside the window).
+    auto single_row = [&](auto df, int64_t r) {
+        const rsrc_t ir = in_row(r);
+        const int64_t u = r - (K - 1);
+        bwd_row<E, K, decltype(df)::value>(st, bld8<E, LFM2SC_BWD_NT>(dy_row(r), o.b), bld8<E, LFM2SC_BWD_NT>(ir, o.b),
+                                           bld8<E, LFM2SC_BWD_NT>(ir, o.c), bld8<E, LFM2SC_BWD_NT>(ir, o.x),
+                                           din_row(r), u >= lo, u, fg, din_row(u >= lo ? u : r), o);
+        if constexpr (K > 1)
+            if (want_dinit && r == K - 2) store_dinit<E, K>(st, a, sp.seq, ch0, T);
+    };
+    // With a final-state gradient, the row that emits the first of the last K
+    // tokens (the sequence's last row) is taken after the batched rows; the
+    // later K-1 of them are emitted by the rows past the window.
+    const int64_t main_hi = (a.dfinal != nullptr && hi == T && hi > lo) ? hi - 1 : hi;
 
     // Rows whose u = r-K+1 is still before the window: no dB/dxv emitted.
     int64_t r = lo;
-    const int64_t head_end = (lo + K - 1 < hi) ? lo + K - 1 : hi;
-    for (; r < head_end; ++r) {
-        const rsrc_t ir = in_row(r);
-        bwd_row<E, K>(st, bld8<E, LFM2SC_BWD_NT>(dy_row(r), o.b), bld8<E, LFM2SC_BWD_NT>(ir, o.b),
-                      bld8<E, LFM2SC_BWD_NT>(ir, o.c), bld8<E, LFM2SC_BWD_NT>(ir, o.x), din_row(r), false, r, fg,
-                      din_row(r), o);
-        if constexpr (K > 1)
-            if (want_dinit && r == K - 2) store_dinit<E, K>(st, a, sp.seq, ch0, T);
-    }
+    const int64_t head_end = (lo + K - 1 < main_hi) ? lo + K - 1 : main_hi;
+    for (; r < head_end; ++r) single_row(std::false_type{}, r);
     // Steady state: batches of U rows, all loads of a batch issued together.
-    for (; r + U <= hi; r += U) {
+    for (; r + U <= main_hi; r += U) {
         Raw8<E> rdy[U], rb[U], rc[U], rx[U];
         load_batch(rdy, rb, rc, rx, r);
         use_batch(rdy, rb, rc, rx, r);
     }
     // Remainder (< U rows): one partial batch, all its loads issued together.
-    if (r < hi) {
-        const int n = (int)(hi - r);
+    if (r < main_hi) {
+        const int n = (int)(main_hi - r);
         Raw8<E> rdy[U], rb[U], rc[U], rx[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -310,12 +321,13 @@ __device__ __forceinline__ void bwd_window(const BackwardArgs<E>& a, const SeqSp
         for (int u = 0; u < U; ++u) {
             if (u < n) {
                 const int64_t rr = r + u;
-                bwd_row<E, K>(st, rdy[u], rb[u], rc[u], rx[u], din_row(rr), true, rr - (K - 1), fg,
-                              din_row(rr - (K - 1)), o);
+                bwd_row<E, K, false>(st, rdy[u], rb[u], rc[u], rx[u], din_row(rr), true, rr - (K - 1), fg,
+                                     din_row(rr - (K - 1)), o);
             }
         }
-        r = hi;
+        r = main_hi;
     }
+    if (r < hi) single_row(std::true_type{}, r++);
     // K-1 rows past the window: g only, from the next rows of the sequence.
     if constexpr (K > 1) {
         for (; r < hi + K - 1; ++r) {
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(kSmallBlock) void dinit_empty_kernel(const int32_t*
 
 // fp32 I/O carries fp64 state: fewer rows in flight keep it in registers.
 template <typename E, int K> constexpr int bwd_unroll() {
-    return sizeof(typename BwdAcc<E>::type) == 8 ? (K >= 4 ? 1 : 2) : LFM2SC_BWD_U;
+    return sizeof(typename BwdAcc<E>::type) == 8 ? (K >= 3 ? 1 : 2) : LFM2SC_BWD_U;
 }
 
 template <typename E, int K>
