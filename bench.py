@@ -11,7 +11,7 @@ the measured step time (GB/s); the roofline object reports the backward call
 (its dominant launch) against the MI355X HBM peak; cpu_baseline times the fp64
 oracle on a bounded channel sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
        python bench.py --calibrate-copy   (plain device copy of known size, for counter scaling)
 """
 import argparse
@@ -214,7 +214,9 @@ def main():
     ap.add_argument("--T", type=int, default=65536)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-channels", type=int, default=2048)
-    ap.add_argument("--extra", action="store_true", help="also time decode, ragged prefill and verify")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the decode, ragged prefill and verify figures (graph replay, a few seconds)")
+    ap.add_argument("--extra", dest="extra", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
