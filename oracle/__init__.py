@@ -45,6 +45,7 @@ def _load():
     for name in ("oracle_prefill", "oracle_decode", "oracle_verify", "oracle_commit", "oracle_backward"):
         getattr(lib, name).restype = _int
     _lib = lib
+    lib.oracle_in_proj.argtypes = [_i64, _int, _int, _dp, _i64, _dp, _dp]
     return lib
 
 
@@ -165,3 +166,22 @@ def backward(inp, cu, w, dy, pool=None, slot_idx=None, bias=None, d_final=None, 
                                    _p(p), 0 if p is None else p.shape[0], _p(sl, _ip), _p(dy), _p(dF),
                                    _p(d_in), _p(dW), _p(dbias), _p(d_init)), "backward")
     return (d_in, dW, dbias, d_init) if full else (d_in, dW)
+
+
+def in_proj(x, W_in):
+    """x [rows, >=D] @ W_in[3H, D]^T -> [rows, 3H] (B | C | xv), fp64."""
+    x, W_in = f64(x), f64(W_in)
+    n_out, D = W_in.shape
+    rows = x.shape[0]
+    out = np.full((rows, n_out), np.nan)
+    _check(_load().oracle_in_proj(rows, D, n_out, _p(x), x.shape[1] if x.ndim == 2 else D, _p(W_in), _p(out)),
+           "in_proj")
+    return out
+
+
+def fused_prefill(x, W_in, cu, w, pool=None, slot_idx=None, bias=None):
+    """in_proj followed by the ragged prefill.  Returns (y [rows, H], new_pool or None, in_proj [rows, 3H])."""
+    ip = in_proj(x, W_in)
+    y, newpool = prefill(ip, cu, w, pool, slot_idx, bias)
+    return y, newpool, ip
+

@@ -316,3 +316,25 @@ int oracle_backward(int H, int K, int64_t total_T,
     }
     return fail ? -1 : 0;
 }
+
+/* MAX Pipelines LFM2 article, "ShortConv implementation (LFM2ShortConv)": the
+ * in_proj layer projects the hidden state into the three parts b, c, xv.  The
+ * plain definition of that linear map, one dot product per output element. */
+int oracle_in_proj(int64_t rows, int D, int n_out,
+                   const double* x, int64_t x_stride, const double* W_in,
+                   double* out) {
+    if (rows < 0 || D <= 0 || n_out <= 0 || x_stride < D) return -1;
+    if (rows == 0) return 0;
+    if (!x || !W_in || !out) return -1;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+    for (int64_t t = 0; t < rows; ++t) {
+        const double* xr = x + t * x_stride;
+        for (int j = 0; j < n_out; ++j) {
+            const double* wr = W_in + (int64_t)j * D;
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d) acc += xr[d] * wr[d];
+            out[t * n_out + j] = acc;
+        }
+    }
+    return 0;
+}

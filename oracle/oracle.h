@@ -49,6 +49,11 @@
  *     article's weight-name mapping carries a conv bias and SGLang's excerpt
  *     passes one to its conv update; the released LFM2 checkpoints are
  *     bias-free (Liger-Kernel PR, "Gated short convolution").
+ *   - in_proj (the fused forward only): a linear map of the hidden state x
+ *     [rows][D] by a weight W_in [3H][D] in the usual out-by-in layout, no
+ *     bias: column j of the in_proj row is sum_d x[d] * W_in[j][d].  The MAX
+ *     article says only that in_proj projects the hidden state into the three
+ *     parts; it names no in_proj bias.
  *   - Backward: the gradient of the initial state is returned on request, and a
  *     gradient arriving at the returned final state may be given (chunked
  *     training: chunk c+1's initial-state gradient is chunk c's final-state
@@ -65,6 +70,7 @@
  *   dW     [H][K]
  *   bias   [H] (NULL = no bias), dbias [H]
  *   d_final, d_init  [N][H][K]  (gradients of each sequence's final / initial state)
+ *   x      [rows][x_stride]    hidden states (D used), W_in [3H][D]
  *
  * Every function returns 0 on success and -1 if an argument is out of range
  * (the oracle checks what it needs to stay in bounds; it is not a validator).
@@ -129,6 +135,12 @@ int oracle_backward(int H, int K, int64_t total_T,
                     const double* pool, int64_t num_slots, const int32_t* slot_idx,
                     const double* dy, const double* d_final,
                     double* d_in, double* dW, double* dbias, double* d_init);
+
+/* in_proj = x W_in^T for the fused forward: out[t][j] = sum over d (ascending) of
+ * x[t][d] * W_in[j][d], for t < rows, j < n_out; out is dense [rows][n_out]. */
+int oracle_in_proj(int64_t rows, int D, int n_out,
+                   const double* x, int64_t x_stride, const double* W_in,
+                   double* out);
 
 #ifdef __cplusplus
 }
