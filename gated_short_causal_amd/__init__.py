@@ -14,6 +14,8 @@ from .binding import (  # noqa: F401
     lfm2sc_backward_workspace_bytes,
     lfm2sc_commit_window,
     lfm2sc_decode_step,
+    lfm2sc_fused_prefill,
+    lfm2sc_fused_prefill_workspace_bytes,
     lfm2sc_prefill_ragged,
     lfm2sc_verify_window,
 )

@@ -162,5 +162,33 @@ def lfm2sc_backward(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, workspace,
     return d_in_proj, dW
 
 
+def lfm2sc_fused_prefill_workspace_bytes(dtype, H, K, num_seqs, with_pool) -> int:
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.lib().lfm2sc_fused_prefill_workspace_bytes(code, H, K, num_seqs, int(bool(with_pool))))
+
+
+def lfm2sc_fused_prefill(x, W_in, cu_seqlens, weight, y, state_pool=None, slot_idx=None, bias=None,
+                         in_proj_out=None, workspace=None):
+    """in_proj (x @ W_in^T, on the matrix cores) fused with the ShortConv prefill.  x [rows, >=D] bf16,
+    W_in [3H, D] bf16.  Writes y (and in_proj_out when given); with a pool, the final states go through
+    `workspace` (lfm2sc_fused_prefill_workspace_bytes bytes) into the slots."""
+    H, K = _hk(weight)
+    if W_in.dim() != 2 or not W_in.is_contiguous() or W_in.shape[0] != 3 * H:
+        raise ValueError(f"W_in must be a contiguous [{3 * H}, D] tensor")
+    D = W_in.shape[1]
+    _i32(cu_seqlens, "cu_seqlens"); _i32(slot_idx, "slot_idx")
+    num_slots = slot_stride = 0
+    if state_pool is not None:
+        slot_stride = _pool_stride(state_pool, H, K)
+        num_slots = state_pool.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    io_stride = 0 if in_proj_out is None else _rows(in_proj_out, "in_proj_out")
+    _check(_lib.lib().lfm2sc_fused_prefill(
+        _dtype_code(weight), H, K, D, _ptr(x), _rows(x, "x"), x.shape[0], _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        _ptr(W_in), _ptr(weight), _ptr(bias), _ptr(state_pool), num_slots, slot_stride, _ptr(slot_idx),
+        _ptr(y), _rows(y, "y"), _ptr(in_proj_out), io_stride, _ptr(workspace), ws_bytes, _stream(x.device)))
+    return y
+
+
 def abi_version() -> int:
     return int(_lib.lib().lfm2sc_abi_version())

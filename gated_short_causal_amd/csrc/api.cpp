@@ -365,4 +365,64 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
                                 dW, dbias, d_init_state, workspace, s);
 }
 
-}  // extern "C"
+size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seqs, int with_pool) {
+    if (dtype != LFM2SC_BF16 || H < 64 || H % 64 != 0 || H > kMaxH || K < 1 || K > 4 || num_seqs < 0) return 0;
+    if (!with_pool) return 0;
+    return ((size_t)num_seqs * (size_t)H * (size_t)K * 2 + 255) / 256 * 256;
+}
+
+int lfm2sc_fused_prefill(int dtype, int H, int K, int D, const void* x, int64_t x_stride, int64_t total_T,
+                         const int32_t* cu_seqlens, int num_seqs, const void* W_in, const void* weight,
+                         const void* bias, void* state_pool, int64_t num_slots, int64_t slot_stride,
+                         const int32_t* slot_idx, void* y, int64_t y_stride, void* in_proj_out, int64_t io_stride,
+                         void* workspace, size_t workspace_bytes_, void* stream) {
+    const char* fn = "lfm2sc_fused_prefill";
+    TRY(check_common(fn, dtype, H, K, bias));
+    if (dtype != LFM2SC_BF16) return fail(LFM2SC_ERR_UNSUPPORTED, "%s: only LFM2SC_BF16 is supported", fn);
+    if (H % 64 != 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: H=%d is not a multiple of 64", fn, H);
+    if (D < 64 || D % 64 != 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: D=%d is not a positive multiple of 64", fn, D);
+    if ((int64_t)3 * H * D * 2 >= kMaxRows)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: W_in of 3H x D = %d x %d is 2 GiB or more", fn, 3 * H, D);
+    if (num_seqs < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d is negative", fn, num_seqs);
+    if (total_T < 0 || total_T >= kMaxRows)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: total_T=%lld outside [0, 2^31)", fn, (long long)total_T);
+    TRY(check_stride(fn, "x_stride", x_stride, D));
+    if (x_stride * 2 * 256 >= kMaxRows)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: x_stride=%lld too large", fn, (long long)x_stride);
+    TRY(check_stride(fn, "y_stride", y_stride, H));
+    if (in_proj_out != nullptr) TRY(check_stride(fn, "io_stride", io_stride, 3 * (int64_t)H));
+    if (num_seqs == 0 || total_T == 0) return ok();   // no token: nothing computed, no state changes
+    TRY(check_ptr(fn, "x", x, 16));
+    TRY(check_ptr(fn, "cu_seqlens", cu_seqlens, 4));
+    TRY(check_ptr(fn, "W_in", W_in, 16));
+    TRY(check_ptr(fn, "weight", weight, 16));
+    TRY(check_ptr(fn, "y", y, 16));
+    if (in_proj_out != nullptr) TRY(check_ptr(fn, "in_proj_out", in_proj_out, 16));
+    if (state_pool != nullptr) {
+        TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
+        const size_t need = lfm2sc_fused_prefill_workspace_bytes(dtype, H, K, num_seqs, 1);
+        if (workspace == nullptr || workspace_bytes_ < need)
+            return fail(LFM2SC_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace,
+                        workspace_bytes_, need);
+        if (!aligned(workspace, 16)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: workspace is not 16-byte aligned", fn);
+    }
+    if (fused_tiles(total_T, H, K) >= (1 << 30))
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many tokens for one launch", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TRY(device_check(fn, s, state_pool ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens, total_T, nullptr, 0));
+    FusedArgs a;
+    a.x = static_cast<const uint16_t*>(x); a.x_stride = x_stride; a.total_T = total_T; a.D = D;
+    a.W = static_cast<const uint16_t*>(W_in);
+    a.cu = cu_seqlens; a.N = num_seqs;
+    a.w = static_cast<const uint16_t*>(weight); a.bias = static_cast<const uint16_t*>(bias);
+    a.pool = static_cast<uint16_t*>(state_pool); a.num_slots = num_slots; a.slot_stride = slot_stride;
+    a.slot_idx = slot_idx;
+    a.y = static_cast<uint16_t*>(y); a.y_stride = y_stride;
+    a.io = static_cast<uint16_t*>(in_proj_out); a.io_stride = io_stride;
+    a.fin = state_pool != nullptr ? static_cast<uint16_t*>(workspace) : nullptr;
+    a.H = H;
+    a.tiles_m = a.tiles_n = 0;
+    return launched(fn, launch_fused_prefill(a, K, s));
+}
+
+}  // extern "C\"

@@ -64,6 +64,26 @@ struct BackwardArgs {
     int ntiles;
 };
 
+// Fused in_proj GEMM + ShortConv forward (bf16 only).  x [total_T][x_stride]
+// (D used), W [3H][D]; y [total_T][y_stride]; io: optional in_proj output
+// [total_T][io_stride] (B | C | xv, bf16); fin: [N][H][K] staging for the final
+// states when a pool is given (then installed into the slots), else nullptr.
+struct FusedArgs {
+    const uint16_t* x; int64_t x_stride; int64_t total_T; int D;
+    const uint16_t* W;
+    const int32_t* cu; int N;
+    const uint16_t* w; const uint16_t* bias;
+    uint16_t* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    uint16_t* y; int64_t y_stride;
+    uint16_t* io; int64_t io_stride;
+    uint16_t* fin;
+    int H;
+    int tiles_m, tiles_n;   // set by the launcher
+};
+hipError_t launch_fused_prefill(const FusedArgs& a, int K, hipStream_t s);
+// Tiles of a fused launch (host-side size checks).
+int64_t fused_tiles(int64_t total_T, int H, int K);
+
 // Rows of dW/dbias partials (one per workgroup window, H*(K+1) elements each)
 // a backward launch of these sizes writes to its workspace, and the bytes of
 // one partial element; the launcher and the workspace-size query share this.

@@ -135,3 +135,66 @@ def random_case(seed: int, lens, H: int, K: int, dtype, slots: int = 0, with_dy:
         slot_idx = torch.randperm(slots, generator=g)[:N].to(torch.int32)
     dy = _normal(g, (total, H), dtype) if with_dy else None
     return Workload("random_case", dtype, H, K, inp, w, cu=cu, pool=pool, slot_idx=slot_idx, dy=dy)
+
+
+@dataclass
+class FusedWorkload:
+    """Inputs of the fused in_proj + ShortConv forward: hidden states x [rows, >=D], in_proj weight W_in [3H, D]
+    (rows 0..H-1 give B, H..2H-1 C, 2H..3H-1 xv), conv weight w [H, K], optional bias, ragged offsets and slots."""
+    name: str
+    H: int
+    K: int
+    D: int
+    x: torch.Tensor
+    W_in: torch.Tensor
+    w: torch.Tensor
+    cu: torch.Tensor
+    bias: Optional[torch.Tensor] = None
+    pool: Optional[torch.Tensor] = None
+    slot_idx: Optional[torch.Tensor] = None
+
+    def to(self, device):
+        out = FusedWorkload(**{k: getattr(self, k) for k in self.__dataclass_fields__})
+        for k in ("x", "W_in", "w", "cu", "bias", "pool", "slot_idx"):
+            v = getattr(out, k)
+            if v is not None:
+                setattr(out, k, v.to(device))
+        return out
+
+
+def fused_case(seed: int, lens, H: int, K: int, D: int, slots: int = 0, bias: bool = False, x_pad: int = 0,
+               tail_rows: int = 0) -> FusedWorkload:
+    """bf16 hidden states x ~ N(0,1) and W_in ~ N(0, 1/D) (so in_proj entries are about N(0,1), like the
+    other workloads' in_proj rows), w ~ U(-0.5,0.5), optional bias ~ N(0,1) and pool ~ N(0,1).  `tail_rows`
+    extra rows after the last sequence belong to no sequence; `x_pad` extra columns pad the x rows."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(list(lens), dtype=torch.int64)
+    N = lens.numel()
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    if N:
+        cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    rows = int(cu[-1]) + tail_rows
+    dt = torch.bfloat16
+    x = _normal(g, (rows, D + x_pad), dt)
+    W_in = (torch.randn((3 * H, D), generator=g, dtype=torch.float32) * D ** -0.5).to(dt)
+    w = _uniform_half(g, (H, K), dt)
+    b = _normal(g, (H,), dt) if bias else None
+    pool = slot_idx = None
+    if slots:
+        pool = _normal(g, (slots, H, K), dt)
+        slot_idx = torch.randperm(slots, generator=g)[:N].to(torch.int32)
+    return FusedWorkload("fused_case", H, K, D, x, W_in, w, cu, bias=b, pool=pool, slot_idx=slot_idx)
+
+
+def fused_train_lfm2(seed: int = 6, T: int = 65536, H: int = H_LFM2, K: int = K_LFM2, D: int = H_LFM2) -> FusedWorkload:
+    """Training forward of one ShortConv layer through the fused path: one sequence of T tokens, hidden size
+    D = 2048 (LFM2-1.2B: hidden size = conv_dim), zero initial state."""
+    return fused_case(seed, [T], H, K, D)
+
+
+def fused_ragged_lfm2(seed: int = 7, N: int = 8, lo: int = 64, hi: int = 2048, H: int = H_LFM2, K: int = K_LFM2,
+                      D: int = H_LFM2) -> FusedWorkload:
+    """Ragged prefill through the fused path: N sequences with lengths uniform on [lo, hi], one pool slot each."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(lo, hi + 1, (N,), generator=g).tolist()
+    return fused_case(seed + 1000, lens, H, K, D, slots=N)

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LFM2SC_ABI_VERSION 2
+#define LFM2SC_ABI_VERSION 3
 
 enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
 
@@ -227,6 +227,50 @@ const char* lfm2sc_status_string(int status);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* lfm2sc_last_error(void);
+
+/*
+ * Fused in_proj + ShortConv forward (bf16 only): the in_proj GEMM runs on the
+ * matrix cores and the gated conv of lfm2sc_prefill_ragged runs in its
+ * epilogue, so in_proj never has to be written to memory and read back.
+ *
+ * Passage: MAX Pipelines LFM2 article, "ShortConv implementation
+ * (LFM2ShortConv)": in_proj projects each token's hidden state into b, c and
+ * xv, which then go through the gated conv.  Reading: in_proj is the linear
+ * map in_proj[t][j] = sum_d x[t][d] * W_in[j][d] with no bias (the article
+ * names none).
+ *
+ * x           [total_T][x_stride] bf16 hidden states (the first D columns).
+ * W_in        [3H][D] bf16, row-major (the usual out-by-in weight layout):
+ *             rows [0, H) produce B, [H, 2H) C, [2H, 3H) xv.
+ * cu_seqlens, weight, bias, state_pool, num_slots, slot_stride, slot_idx, y:
+ *             as in lfm2sc_prefill_ragged (same state semantics).
+ * in_proj_out [total_T][io_stride] bf16, or NULL: when given, receives
+ *             B | C | xv rounded to bf16 (the in_proj the backward takes).
+ * workspace   needed only when state_pool is given: at least
+ *             lfm2sc_fused_prefill_workspace_bytes(...) bytes, 16-byte
+ *             aligned.  The final states are staged there and a second kernel
+ *             installs them into the slots once every tile has read its
+ *             initial states.
+ * Requirements beyond the shared ones: dtype LFM2SC_BF16 (else
+ * LFM2SC_ERR_UNSUPPORTED); H % 64 == 0, D % 64 == 0, 3H*D*2 < 2^31 and
+ * 256*x_stride*2 < 2^31 (else LFM2SC_ERR_BAD_SHAPE); x_stride >= D and
+ * io_stride >= 3H, multiples of 8.
+ * Accuracy: B, C and xv are fp32 sums over D and are not rounded before the
+ * conv, so y and the final states carry one bf16 rounding of an fp32 result:
+ * within the bf16 tolerance of the exact value, but not bit-equal to running
+ * a GEMM into bf16 in_proj and then lfm2sc_prefill_ragged.
+ */
+int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
+                         const void* x, int64_t x_stride, int64_t total_T,
+                         const int32_t* cu_seqlens, int num_seqs,
+                         const void* W_in, const void* weight, const void* bias,
+                         void* state_pool, int64_t num_slots, int64_t slot_stride,
+                         const int32_t* slot_idx,
+                         void* y, int64_t y_stride, void* in_proj_out, int64_t io_stride,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of lfm2sc_fused_prefill (0 when with_pool is 0). */
+size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seqs, int with_pool);
 
 /* LFM2SC_ABI_VERSION of the loaded library. */
 int lfm2sc_abi_version(void);

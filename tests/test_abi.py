@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
     for n in names:
         assert hasattr(L, n), n
@@ -183,3 +183,48 @@ def test_binding_names_match_c_abi():
     for n in ("lfm2sc_prefill_ragged", "lfm2sc_decode_step", "lfm2sc_verify_window", "lfm2sc_commit_window",
               "lfm2sc_backward", "lfm2sc_backward_workspace_bytes"):
         assert callable(getattr(g, n)) and n in _lib.SIGNATURES
+
+
+def _fused(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, D=2048, x=P, x_stride=2048, total_T=4096, cu=P, N=1, W=P, w=P, bias=None,
+             pool=None, num_slots=0, slot_stride=0, slot_idx=None, y=P, y_stride=2048, io=None, io_stride=0,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.lfm2sc_fused_prefill(a["dtype"], a["H"], a["K"], a["D"], a["x"], a["x_stride"], a["total_T"], a["cu"],
+                                  a["N"], a["W"], a["w"], a["bias"], a["pool"], a["num_slots"], a["slot_stride"],
+                                  a["slot_idx"], a["y"], a["y_stride"], a["io"], a["io_stride"], a["ws"],
+                                  a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), UNSUP), (dict(dtype=2), UNSUP), (dict(K=5), UNSUP), (dict(bias=MIS), ALIGN),
+    (dict(H=1000), SHAPE), (dict(H=72), SHAPE), (dict(D=0), SHAPE), (dict(D=1000), SHAPE), (dict(D=32), SHAPE),
+    (dict(H=8192, D=65536, x_stride=65536), SHAPE),
+    (dict(N=-1), SHAPE), (dict(total_T=-1), SHAPE), (dict(total_T=1 << 31), SHAPE),
+    (dict(x_stride=2040), SHAPE), (dict(x_stride=2052), ALIGN), (dict(x_stride=1 << 22), SHAPE),
+    (dict(y_stride=2047), SHAPE), (dict(io=P, io_stride=6000), SHAPE), (dict(io=P, io_stride=6148), ALIGN),
+    (dict(x=None), NULLP), (dict(x=MIS), ALIGN), (dict(cu=None), NULLP), (dict(W=None), NULLP), (dict(W=MIS), ALIGN),
+    (dict(w=None), NULLP), (dict(y=None), NULLP), (dict(io=MIS, io_stride=6144), ALIGN),
+    (dict(pool=P, num_slots=4, slot_stride=6144, slot_idx=None), NULLP),
+    (dict(pool=P, num_slots=4, slot_stride=6000, slot_idx=P), SHAPE),
+    (dict(pool=P, num_slots=4, slot_stride=6144, slot_idx=P), WS),
+    (dict(pool=P, num_slots=4, slot_stride=6144, slot_idx=P, ws=P, ws_bytes=100), WS),
+    (dict(pool=P, num_slots=4, slot_stride=6144, slot_idx=P, ws=MIS, ws_bytes=1 << 20), ALIGN),
+])
+def test_fused_rejects(L, kw, code):
+    assert _fused(L, **kw) == code
+    assert L.lfm2sc_last_error().decode().startswith("lfm2sc_fused_prefill")
+
+
+def test_fused_no_work_is_ok_without_launch(L):
+    assert _fused(L, N=0, x=None, cu=None, W=None, y=None) == OK
+    assert _fused(L, total_T=0, x=None, cu=None, W=None, y=None) == OK
+
+
+def test_fused_workspace_bytes(L):
+    assert L.lfm2sc_fused_prefill_workspace_bytes(0, 2048, 3, 8, 0) == 0
+    assert L.lfm2sc_fused_prefill_workspace_bytes(0, 2048, 3, 8, 1) == 8 * 2048 * 3 * 2
+    assert L.lfm2sc_fused_prefill_workspace_bytes(0, 64, 1, 1, 1) == 256
+    assert L.lfm2sc_fused_prefill_workspace_bytes(1, 2048, 3, 8, 1) == 0     # fp32 unsupported
+    assert L.lfm2sc_fused_prefill_workspace_bytes(0, 72, 3, 8, 1) == 0       # H % 64 != 0
+

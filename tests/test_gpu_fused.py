@@ -1,0 +1,148 @@
+"""GPU parity of the fused in_proj + ShortConv forward (lfm2sc_fused_prefill, through the C ABI) against the fp64
+oracle (oracle.fused_prefill: the in_proj dot products, then the ShortConv prefill).
+
+B, C and xv stay in fp32 inside the kernel, so y, the final states and the optional in_proj output carry one bf16
+rounding of an fp32 result: they are compared within the bf16 tolerance (abs-or-rel 2e-2), and slots the call must
+not touch are compared bit for bit."""
+import pytest
+import torch
+
+import oracle
+from gated_short_causal_amd import (lfm2sc_fused_prefill, lfm2sc_fused_prefill_workspace_bytes,
+                                    lfm2sc_prefill_ragged)
+from gated_short_causal_amd import workloads as wl
+from tests.parity_util import assert_bits, assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+BF = torch.bfloat16
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _nan(shape):
+    return torch.full(shape, float("nan"), dtype=BF, device=DEV)
+
+
+def _run(c, with_io=False, y_pad=0, io_pad=0):
+    g = c.to(DEV)
+    rows = c.x.shape[0]
+    N = c.cu.numel() - 1
+    y = _nan((rows, c.H + y_pad))[:, : c.H] if y_pad else _nan((rows, c.H))
+    io = None
+    if with_io:
+        io = _nan((rows, 3 * c.H + io_pad))[:, : 3 * c.H] if io_pad else _nan((rows, 3 * c.H))
+    ws = None
+    if c.pool is not None:
+        ws = torch.empty(max(16, lfm2sc_fused_prefill_workspace_bytes(BF, c.H, c.K, N, True)), dtype=torch.uint8,
+                         device=DEV)
+    x = g.x[:, : c.D] if g.x.shape[1] != c.D else g.x
+    lfm2sc_fused_prefill(x, g.W_in, g.cu, g.w, y, g.pool, g.slot_idx, bias=g.bias, in_proj_out=io, workspace=ws)
+    torch.cuda.synchronize()
+    return y.cpu(), (None if io is None else io.cpu()), (None if g.pool is None else g.pool.cpu())
+
+
+def _check(c, y, io, pool, what):
+    x = c.x[:, : c.D]
+    y_ref, p_ref, ip_ref = oracle.fused_prefill(x, c.W_in, c.cu, c.w, c.pool, c.slot_idx, bias=c.bias)
+    covered = int(c.cu[-1])
+    assert_close(y[:covered], y_ref[:covered], BF, f"{what}: y")
+    if covered < y.shape[0]:
+        assert torch.isnan(y[covered:].float()).all(), f"{what}: rows outside every sequence were written"
+    if io is not None:
+        assert_close(io[:covered], ip_ref[:covered], BF, f"{what}: in_proj_out")
+    if pool is not None:
+        assert_close(pool, p_ref, BF, f"{what}: final states")
+        lens = (c.cu[1:] - c.cu[:-1]).tolist()
+        touched = {int(s) for s, n in zip(c.slot_idx.tolist(), lens) if n > 0}
+        for s in range(pool.shape[0]):
+            if s not in touched:
+                assert_bits(pool[s], c.pool[s], f"{what}: slot {s} must be untouched")
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+def test_fused_ragged_pool_bias(K):
+    lens = [37, 1, 0, 300, 5, 2]
+    _say(f"case: fused ragged K={K} lens={lens} H=128 D=192 pool+bias")
+    c = wl.fused_case(500 + K, lens, H=128, K=K, D=192, slots=9, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    _check(c, y, io, pool, f"K={K}")
+
+
+def test_fused_training_shape_no_pool():
+    """One sequence over several row tiles, no pool (zero initial state, no state out), in_proj kept."""
+    _say("case: fused one sequence T=1000 H=256 D=256 no pool")
+    c = wl.fused_case(510, [1000], H=256, K=3, D=256)
+    y, io, pool = _run(c, with_io=True)
+    _check(c, y, io, pool, "train")
+
+
+def test_fused_short_sequences_and_tail_rows():
+    """Many sequences shorter than K in one tile and across a tile boundary, rows after the last sequence,
+    padded x / y / in_proj rows."""
+    lens = [1, 2, 1, 0, 3, 1] * 50
+    _say(f"case: fused {len(lens)} short sequences, tail rows, padded strides")
+    c = wl.fused_case(511, lens, H=64, K=3, D=64, slots=len(lens) + 4, bias=True, x_pad=8, tail_rows=7)
+    y, io, pool = _run(c, with_io=True, y_pad=8, io_pad=16)
+    _check(c, y, io, pool, "short")
+
+
+def test_fused_out_of_range_slots():
+    lens = [4, 9, 2]
+    _say("case: fused out-of-range slot ids")
+    c = wl.fused_case(512, lens, H=64, K=3, D=128, slots=5)
+    c.slot_idx = torch.tensor([1, 5, -2], dtype=torch.int32)
+    y, io, pool = _run(c)
+    # sequences 1 and 2 start from a zero state and write nothing
+    zero = c.pool.clone()
+    zero[:] = 0
+    y_ref_ok, p_ok, _ = oracle.fused_prefill(c.x, c.W_in, c.cu, c.w, c.pool, torch.tensor([1, 2, 3]))
+    y_ref_zero, _, _ = oracle.fused_prefill(c.x, c.W_in, c.cu, c.w, zero, torch.tensor([0, 1, 2]))
+    assert_close(y[:4], y_ref_ok[:4], BF, "valid slot rows")
+    assert_close(y[4:], y_ref_zero[4:], BF, "rows of out-of-range slots")
+    assert_close(pool[1], p_ok[1], BF, "valid slot state")
+    for s in (0, 2, 3, 4):
+        assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
+
+
+def test_fused_lfm2_shape_sampled_channels():
+    """LFM2-1.2B layer shape (H = D = 2048) over 4096 tokens in 3 ragged sequences with a pool; the oracle
+    computes 24 sampled channels (channels are independent once in_proj is formed)."""
+    lens = [1500, 7, 2589]
+    _say("case: fused H=2048 D=2048 T=4096 ragged, sampled channels")
+    c = wl.fused_case(513, lens, H=2048, K=3, D=2048, slots=6, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    chans = torch.tensor([0, 1, 31, 32, 63, 64, 100, 511, 512, 777, 1023, 1024, 1300, 1535, 1536, 1600, 1800,
+                          1983, 2000, 2014, 2031, 2040, 2046, 2047])
+    H = c.H
+    rows = torch.cat([chans, chans + H, chans + 2 * H])
+    y_ref, p_ref, ip_ref = oracle.fused_prefill(c.x, c.W_in[rows], c.cu, c.w[chans], c.pool[:, chans, :],
+                                                c.slot_idx, bias=c.bias[chans])
+    assert_close(y[:, chans], y_ref, BF, "y (sampled)")
+    assert_close(io[:, rows], ip_ref, BF, "in_proj_out (sampled)")
+    assert_close(pool[:, chans, :], p_ref, BF, "final states (sampled)")
+
+
+def test_fused_in_proj_matches_torch_gemm():
+    """The in_proj the fused call hands to the backward against torch's GEMM of the same bf16 operands (fp32
+    accumulation, rounded to bf16).  y is not compared with the unfused path (a bf16 GEMM followed by
+    lfm2sc_prefill_ragged): that path rounds B, C and xv before the conv, so it is itself an approximation whose
+    distance from the fused result is not bounded by one bf16 tolerance; both are checked against the oracle."""
+    lens = [700, 0, 333, 64]
+    _say("case: fused in_proj_out vs torch GEMM")
+    c = wl.fused_case(514, lens, H=512, K=3, D=1024, slots=5, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    g = c.to(DEV)
+    ip = torch.matmul(g.x.float(), g.W_in.float().t()).to(BF).cpu()
+    assert_close(io, ip.double(), BF, "in_proj_out vs torch GEMM")
+    _check(c, y, io, pool, "vs oracle")
+
+
+def test_fused_deterministic():
+    c = wl.fused_case(515, [400, 90], H=128, K=3, D=256, slots=3)
+    a = _run(c, with_io=True)
+    b = _run(c, with_io=True)
+    for u, v, n in zip(a, b, ("y", "in_proj", "pool")):
+        assert_bits(u, v, f"rerun {n}")
