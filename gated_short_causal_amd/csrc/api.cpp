@@ -380,7 +380,8 @@ int lfm2sc_fused_prefill(int dtype, int H, int K, int D, const void* x, int64_t 
     TRY(check_common(fn, dtype, H, K, bias));
     if (dtype != LFM2SC_BF16) return fail(LFM2SC_ERR_UNSUPPORTED, "%s: only LFM2SC_BF16 is supported", fn);
     if (H % 64 != 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: H=%d is not a multiple of 64", fn, H);
-    if (D < 64 || D % 64 != 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: D=%d is not a positive multiple of 64", fn, D);
+    if (D < fused_depth_multiple() || D % fused_depth_multiple() != 0)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: D=%d is not a positive multiple of %d", fn, D, fused_depth_multiple());
     if ((int64_t)3 * H * D * 2 >= kMaxRows)
         return fail(LFM2SC_ERR_BAD_SHAPE, "%s: W_in of 3H x D = %d x %d is 2 GiB or more", fn, 3 * H, D);
     if (num_seqs < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d is negative", fn, num_seqs);

@@ -17,23 +17,30 @@
 // and xv of the same channel and rows in its accumulators.  Consecutive tiles
 // overlap by K-1 rows: a tile outputs rows K-1 .. 255 of the rows it computes,
 // so the conv history of every output row is inside the tile (0.8% extra MFMA
-// work at K = 3).  The reduction runs in stages of kFBK = 64, double-buffered
-// in LDS: the next stage's global loads are in flight while the current stage
-// feeds the matrix cores.
+// work at K = 3).
 //
-// LDS layout.  A stage holds x rows [256][64] and W_in rows [192][64] (bf16,
-// 128 B per row).  16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7):
-// the 16 lanes of a ds_read_b128 quarter (16 consecutive rows, one chunk) and
-// of a ds_write_b128 quarter (2 rows, all chunks) then touch all 64 banks once.
+// Reduction.  Stages of kFBK = 32 along D.  The x rows and W_in rows of a stage
+// go from global memory straight into one slot of a 4-deep LDS ring (buffer
+// loads with an LDS destination, no registers in between), 3 stages ahead of
+// the one being consumed.  The ring slots are separate LDS arrays, so the
+// compiler can tell that a refill never overlaps the slot being read and does
+// not wait for it; the reduction is fully unrolled for the usual hidden sizes
+// (straight-line code keeps the wait counts exact), with a loop for the rest.
+// (Loading each wave's W_in operands straight into registers instead was
+// slower on MI355X: both row halves then fetch them, and the vector-memory
+// path, not LDS, is what this loop runs short of.)
 //
-// Epilogue.  bx of every computed row goes to LDS (fp32, reusing the stage
-// buffers); each lane then forms conv for its own rows from bx of the K-1
-// previous rows (LDS) or, for the first K-1 tokens of a sequence, from the
-// initial state; y = C * conv is rounded once to bf16.  Final states are the
-// last K entries of [initial state | bx]: the tile that holds a sequence's
-// last token writes them to a per-sequence staging block, and a second small
-// kernel installs them into the slots after every tile has read its initial
-// states (a slot may be read by one tile and written by another).
+// Epilogue.  Each lane holds B, C, xv of one channel for runs of 4 consecutive
+// rows; the K-1 rows before a run live in the partner lane (lane ^ 32), or for
+// the first run of the second row half in the other wave (through a small LDS
+// buffer).  y = C * conv is rounded once to bf16 and staged in LDS so that the
+// stores to y are 16-byte row segments.  Final states are the last K entries
+// of [initial state | bx]: the tile that holds a sequence's last token writes
+// them to a per-sequence staging block, and a second small kernel installs
+// them into the slots after every tile has read its initial states (a slot may
+// be read by one tile and written by another).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -41,34 +48,22 @@ namespace lfm2sc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFBM = 256;              // token rows computed per tile
 constexpr int kFNC = 64;               // channels per tile
-constexpr int kFBN = 3 * kFNC;         // GEMM columns per tile (B | C | xv)
-constexpr int kFBK = 32;               // reduction depth per LDS stage
-#ifndef LFM2SC_FUSED_STAGES
-#define LFM2SC_FUSED_STAGES 4
-#endif
-constexpr int kFStages = LFM2SC_FUSED_STAGES;   // LDS ring depth: kFStages-1 stages in flight ahead of the one in use
+constexpr int kFBK = 32;               // reduction depth per stage
+constexpr int kFStages = 4;            // ring depth: 3 stages in flight ahead of the one in use
 constexpr int kFThreads = 256;         // 4 waves
-constexpr int kFRowBytes = kFBK * 2;   // one staged row: 32 bf16 = 64 B = 4 chunks of 16 B
-constexpr int kFStageA = kFBM * kFRowBytes;   // 16 KiB
-constexpr int kFStageB = kFBN * kFRowBytes;   // 12 KiB
-constexpr int kFStage = kFStageA + kFStageB;
-constexpr int kFRing = kFStages * kFStage;    // 112 KiB at 4 stages
+constexpr int kFRowBytes = kFBK * 2;   // one staged x row: 32 bf16 = 64 B = 4 chunks of 16 B
+constexpr int kFStageA = kFBM * kFRowBytes;           // 16 KiB of x rows per stage
+constexpr int kFStageB = 3 * kFNC * kFRowBytes;       // 12 KiB of W_in rows per stage
 // One global->LDS instruction moves 64 lanes x 16 B = 16 staged rows; per stage
-// the 4 waves move 16 A blocks and 12 B blocks, i.e. 4 + 3 per wave.
-constexpr int kFDmaA = kFBM / 16 / 4, kFDmaB = kFBN / 16 / 4, kFDmaPerStage = kFDmaA + kFDmaB;
-// Epilogue buffers, carved from the ring once the reduction is done:
-// bx channel-major [64][kFBxStride] fp32 (rows at offset kFBxPad, so the K-1
-// rows before row 0 exist), then an output staging tile [256][kFOutStride] bf16.
-constexpr int kFBxPad = 4;
-constexpr int kFBxStride = kFBM + kFBxPad;            // 260 floats: lanes 0..15 of a quarter hit distinct banks
-constexpr int kFBxBytes = kFNC * kFBxStride * 4;
-constexpr int kFOutStride = kFNC + 8;                  // 72 bf16 = 144 B per staged output row
-constexpr int kFOutBytes = kFBM * kFOutStride * 2;
-static_assert(kFBxBytes + kFOutBytes <= kFRing, "epilogue buffers must fit in the ring");
+// the 4 waves move 16 x blocks and 12 W_in blocks, 4 + 3 per wave.
+constexpr int kFDmaA = kFBM / 16 / 4, kFDmaB = 3 * kFNC / 16 / 4;
+constexpr int kFVmPerStage = kFDmaA + kFDmaB;
+// Output staging tile [256][kFOutStride] bf16: the two row halves of a wave
+// (hl = 0, 1: rows 4 apart) land 576 B apart, i.e. in different banks.
+constexpr int kFOutStride = kFNC + 8;
 
 template <int K> constexpr int fused_out_rows() { return kFBM - (K - 1); }
 
@@ -95,10 +90,7 @@ template <int n> __device__ __forceinline__ void wait_vm() {
 // Workgroup -> (m, n) tile: XCD-contiguous runs of the linear tile order, in
 // groups of kFGroupM row tiles that sweep every channel tile, so the workgroups
 // an XCD runs at once share x rows and W_in rows in its L2.
-#ifndef LFM2SC_FUSED_GROUP_M
-#define LFM2SC_FUSED_GROUP_M 4
-#endif
-constexpr int kFGroupM = LFM2SC_FUSED_GROUP_M;
+constexpr int kFGroupM = 4;
 __device__ __forceinline__ void fused_tile(int lin, int tiles_m, int tiles_n, int& m, int& n) {
     const int per_group = kFGroupM * tiles_n;
     const int g = lin / per_group;
@@ -112,12 +104,11 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Workgroup barrier between reduction stages without __syncthreads' release
 // fence: that fence waits for every outstanding vector-memory operation, i.e.
-// for the global->LDS loads of the stages still in flight, which would drain
-// the ring at every stage.  It is not needed here: before the barrier each wave
-// has waited (wait_vm) for its own loads of the stage about to be read, and
-// its LDS reads of the buffer about to be refilled were consumed by its MFMAs.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
+// for the loads of the stages still in flight, which would drain the ring at
+// every stage.  It is not needed here: before the barrier each wave has waited
+// (wait_vm) for its own loads of the stage about to be read, and its LDS reads
+// of the slot about to be refilled were consumed by its MFMAs.  The empty asm
+// statements keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -134,12 +125,20 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int K>
+template <int v> using IC = std::integral_constant<int, v>;
+
+// NK: number of kFBK stages along D when it is known at compile time (the
+// reduction is then straight-line code), 0 for the loop form.
+template <int K, int NK>
 __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_prefill_kernel(const FusedArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kFRing];
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kFStageA], ring1[kFStageA], ring2[kFStageA], ring3[kFStageA];
+    __shared__ __attribute__((aligned(16))) uint8_t wring0[kFStageB], wring1[kFStageB], wring2[kFStageB],
+        wring3[kFStageB];
+    __shared__ __attribute__((aligned(16))) uint16_t ost[kFBM * kFOutStride];
     __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
     __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ float s_edge[2][32][4];        // bx of rows 125..127 of each channel (the second half's history)
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
     if (lin >= a.tiles_m * a.tiles_n) return;
@@ -156,8 +155,8 @@ void fused_prefill_kernel(const FusedArgs a) {
     const int n0 = nt * kFNC;                                           // first channel of the tile
 
     // Row -> (sequence, position, length) map of the tile, for the epilogue.  It
-    // is built before any global->LDS load is issued: waiting on a vector load
-    // would also wait on every load issued before it.  The sequence of the
+    // is built before any load of the reduction is issued: waiting on a vector
+    // load would also wait on every load issued before it.  The sequence of the
     // tile's first row comes from a wave-uniform (scalar) search; when that
     // sequence covers every computed row, the map is arithmetic, otherwise each
     // row searches cu_seqlens itself.
@@ -187,10 +186,12 @@ void fused_prefill_kernel(const FusedArgs a) {
     }
 
     // ---------------------------------------------------------------- reduction
-    // Global -> LDS, no registers in between: each lane of a 16-row block
-    // fetches the chunk that the swizzle places at its LDS slot (row lane/4,
-    // position lane%4).  Rows outside [0, T) are clamped to a valid row: they
-    // are never stored and never feed another row's conv history.
+    // x rows: each lane of a 16-row block fetches the chunk that the swizzle
+    // places at its LDS slot (row lane/4, position lane%4).  Rows outside
+    // [0, T) are clamped to a valid row: they are never stored and never feed
+    // another row's conv history.
+    // W_in rows the same way: staged row n of a slot is W_in row
+    // (n / 64) * H + n0 + n % 64 (the B, C, xv rows of the tile's channels).
     const int64_t vlo = row0 < 0 ? 0 : row0;
     const int64_t vhi = (row0 + kFBM < T) ? row0 + kFBM : T;     // > vlo for every launched tile
     const rsrc_t xr = row_rsrc(a.x + vlo * a.x_stride, (uint32_t)((vhi - vlo) * a.x_stride * 2));
@@ -206,12 +207,27 @@ void fused_prefill_kernel(const FusedArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < kFDmaB; ++i) {
-        const int n = (wave + 4 * i) * 16 + brow;                 // staged W_in row: part n / 64, channel n % 64
-        const int64_t wrow = (int64_t)(n / kFNC) * H + n0 + (n % kFNC);
-        woff[i] = (uint32_t)(wrow * a.D * 2) + bchunk;
+        const int n = (wave + 4 * i) * 16 + brow;
+        woff[i] = (uint32_t)(((int64_t)(n / kFNC) * H + n0 + (n % kFNC)) * a.D * 2) + bchunk;
     }
-    auto issue = [&](int kt) {
-        uint8_t* st = smem + (kt % kFStages) * kFStage;
+
+    auto slot = [&](auto u_c) -> uint8_t* {
+        constexpr int u = decltype(u_c)::value;
+        if constexpr (u == 0) return ring0;
+        else if constexpr (u == 1) return ring1;
+        else if constexpr (u == 2) return ring2;
+        else return ring3;
+    };
+    auto wslot = [&](auto u_c) -> uint8_t* {
+        constexpr int u = decltype(u_c)::value;
+        if constexpr (u == 0) return wring0;
+        else if constexpr (u == 1) return wring1;
+        else if constexpr (u == 2) return wring2;
+        else return wring3;
+    };
+    auto issue = [&](auto u_c, int kt) { // loads of stage kt into ring slot u
+        uint8_t* st = slot(u_c);
+        uint8_t* sw = wslot(u_c);
         const uint32_t ko = (uint32_t)kt * kFRowBytes;
 #pragma unroll
         for (int i = 0; i < kFDmaA; ++i)
@@ -219,7 +235,7 @@ void fused_prefill_kernel(const FusedArgs a) {
                                                      0, 0, 0);
 #pragma unroll
         for (int i = 0; i < kFDmaB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + kFStageA + (wave + 4 * i) * 1024), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(sw + (wave + 4 * i) * 1024), 16,
                                                      woff[i] + ko, 0, 0, 0);
     };
 
@@ -231,24 +247,20 @@ void fused_prefill_kernel(const FusedArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const int nk = a.D / kFBK;
-#pragma unroll
-    for (int s = 0; s < kFStages - 1; ++s)
-        if (s < nk) issue(s);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most the later stages already issued are outstanding
-        const int later = min(kFStages - 2, nk - 1 - kt);
-        static_assert(kFStages <= 5, "wait cases below cover up to 3 later stages");
-        if (later >= 3) wait_vm<3 * kFDmaPerStage>();
-        else if (later == 2) wait_vm<2 * kFDmaPerStage>();
-        else if (later == 1) wait_vm<kFDmaPerStage>();
-        else wait_vm<0>();
+    // One stage: wait for its loads (this wave's; `later` stages after it may
+    // still be in flight), meet the workgroup, refill the slot the previous
+    // stage used, then feed the matrix cores from slot u.
+    auto stage = [&](auto u_c, int kt, auto later_c, auto refill_c) {
+        constexpr int u = decltype(u_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<decltype(later_c)::value * kFVmPerStage>();
         stage_barrier();
-        // the buffer of stage kt-1 is free now (every wave is past its reads)
-        if (kt + kFStages - 1 < nk) issue(kt + kFStages - 1);
-        const uint8_t* sa = smem + (kt % kFStages) * kFStage;
-        const uint8_t* sb = sa + kFStageA;
+        if constexpr (decltype(refill_c)::value) issue(IC<(u + kFStages - 1) % kFStages>{}, kt + kFStages - 1);
+        // the refill goes out first: left to itself the scheduler may sink it
+        // below the MFMAs, shortening the prefetch
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* sa = slot(u_c);
+        const uint8_t* sb = wslot(u_c);
 #pragma unroll
         for (int kk = 0; kk < kFBK / 16; ++kk) {
             const int c = kk * 2 + hl;
@@ -265,19 +277,66 @@ void fused_prefill_kernel(const FusedArgs a) {
                 for (int j = 0; j < 3; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Four stages at a time (ring slots 0..3); the last group only refills
+    // once (the final stage) and then drains the ring.
+    auto group = [&](int kb) {
+        stage(IC<0>{}, kb + 0, IC<2>{}, std::true_type{});
+        stage(IC<1>{}, kb + 1, IC<2>{}, std::true_type{});
+        stage(IC<2>{}, kb + 2, IC<2>{}, std::true_type{});
+        stage(IC<3>{}, kb + 3, IC<2>{}, std::true_type{});
+    };
+    auto last_group = [&](int kb) {
+        stage(IC<0>{}, kb + 0, IC<2>{}, std::true_type{});
+        stage(IC<1>{}, kb + 1, IC<2>{}, std::false_type{});
+        stage(IC<2>{}, kb + 2, IC<1>{}, std::false_type{});
+        stage(IC<3>{}, kb + 3, IC<0>{}, std::false_type{});
+    };
+    static_assert(kFStages == 4, "the stage groups above are written for a 4-deep ring");
+    issue(IC<0>{}, 0);
+    issue(IC<1>{}, 1);
+    issue(IC<2>{}, 2);
+    if constexpr (NK > 0) {
+        static_assert(NK % kFStages == 0 && NK >= kFStages, "whole stage groups");
+#pragma unroll
+        for (int kb = 0; kb + kFStages < NK; kb += kFStages) group(kb);
+        last_group(NK - kFStages);
+    } else {
+        const int nk = a.D / kFBK;      // a multiple of kFStages, at least kFStages (checked on the host)
+        int kb = 0;
+        for (; kb + kFStages < nk; kb += kFStages) group(kb);
+        last_group(kb);
     }
-    __syncthreads();   // every wave is done with the ring; its space now holds the epilogue buffers
 
     // ---------------------------------------------------------------- epilogue
     // Accumulator register r of row tile i holds computed row
-    // R = wm*128 + i*32 + 8*(r/4) + 4*hl + (r%4) of channel n0 + lcn: lane-local
-    // runs of 4 consecutive rows ("quads"), quad (i, g = r/4) starting at
-    // R0 = wm*128 + i*32 + 8g + 4hl.
-    float* bxT = reinterpret_cast<float*>(smem);                       // [64][kFBxStride], row R at kFBxPad + R
-    uint16_t* ost = reinterpret_cast<uint16_t*>(smem + kFBxBytes);     // [256][kFOutStride] bf16
+    // R = wm*128 + i*32 + 8*(r/4) + 4*hl + (r%4) of channel ch = n0 + lcn:
+    // lane-local runs of 4 consecutive rows ("quads"), quad (i, g = r/4)
+    // starting at R0 = wm*128 + i*32 + 8g + 4hl.  The K-1 rows before a quad
+    // end the partner lane's (lane ^ 32) quad: the same quad for hl = 1, the
+    // previous one for hl = 0 (for the wave's first quad: the other wave of
+    // the same channels, rows 125..127, or rows before the tile for wm = 0,
+    // which are never outputs).
     const int lcn = wn * 32 + q;
     const int ch = n0 + lcn;
-    float* bxc = bxT + lcn * kFBxStride + kFBxPad;
+    float bx[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bx[i][r] = acc[i][0][r] * acc[i][2][r];
+    // tail[i][g][m]: the partner's rows 4g + 4 - (K-1) + m of its tile i
+    float tail[4][4][K > 1 ? K - 1 : 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) tail[i][g][m] = __shfl_xor(bx[i][4 * g + 4 - (K - 1) + m], 32);
+    if (wm == 0 && hl == 1) {
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) s_edge[wn][q][m] = bx[3][12 + 4 - (K - 1) + m];
+    }
 
     // Output rows of the tile go out through `ost` with 16-byte stores: chunk
     // (row, cc) holds channels n0 + 8cc .. +8 of computed row `row`.
@@ -309,19 +368,7 @@ void fused_prefill_kernel(const FusedArgs a) {
             flush_rows(a.io + (int64_t)j * H, a.io_stride, false);
         }
     }
-
-    // bx of every computed row, channel-major
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
-            f32x4 v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = acc[i][0][4 * g + j] * acc[i][2][4 * g + j];
-            *reinterpret_cast<f32x4*>(bxc + R0) = v;
-        }
-    lds_barrier();
+    lds_barrier();                  // s_edge written
 
     float wk[K];
 #pragma unroll
@@ -330,69 +377,74 @@ void fused_prefill_kernel(const FusedArgs a) {
     // Entry idx (1 <= idx < K) of sequence seq's initial state for this channel.
     auto s0 = [&](int seq, int idx) -> float {
         if (a.pool == nullptr) return 0.f;
-        const int64_t slot = a.slot_idx[seq];
-        if (!slot_ok(slot, a.num_slots)) return 0.f;
-        return bf16_val(a.pool[slot * a.slot_stride + (int64_t)ch * K + idx]);
+        const int64_t slot_id = a.slot_idx[seq];
+        if (!slot_ok(slot_id, a.num_slots)) return 0.f;
+        return bf16_val(a.pool[slot_id * a.slot_stride + (int64_t)ch * K + idx]);
+    };
+    // hx[m] = bx of row R0 - (K-1) + m for quad (i, g): K-1 history rows, then the quad's own 4
+    auto history = [&](int i, int g, float* hx) {
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) {
+            float prev;
+            if (g > 0) prev = tail[i][g - 1][m];
+            else if (i > 0) prev = tail[i - 1][3][m];
+            else prev = wm == 1 ? s_edge[wn][q][m] : 0.f;
+            hx[m] = hl ? tail[i][g][m] : prev;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hx[K - 1 + j] = bx[i][4 * g + j];
     };
     // One sequence covers every computed row (and does not end inside the tile
     // when final states are wanted): no per-row sequence logic.
     const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
     const bool simple = p0 >= 0 && pl == p0 + kFBM - 1 && !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
-
     if (simple) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
                 float hx[K - 1 + 4];
-#pragma unroll
-                for (int k = 0; k < K - 1; ++k) hx[k] = bxc[R0 - (K - 1) + k];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) hx[K - 1 + j] = acc[i][0][4 * g + j] * acc[i][2][4 * g + j];
+                history(i, g, hx);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);   // same order as the general path
+                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
 #pragma unroll
                     for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], hx[j + k], conv);
                     stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
                 }
             }
     } else {
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 4; ++i)
-    #pragma unroll
+#pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
-                // bx of rows R0-(K-1) .. R0+3 of this channel: K-1 from LDS, 4 from registers
                 float hx[K - 1 + 4];
-    #pragma unroll
-                for (int k = 0; k < K - 1; ++k) hx[k] = bxc[R0 - (K - 1) + k];
-    #pragma unroll
-                for (int j = 0; j < 4; ++j) hx[K - 1 + j] = acc[i][0][4 * g + j] * acc[i][2][4 * g + j];
+                history(i, g, hx);
                 const int4 p = *reinterpret_cast<const int4*>(s_pos + R0);
                 const int pos4[4] = {p.x, p.y, p.z, p.w};
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int row = R0 + j;
                     const int pos = pos4[j];
                     float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
-    #pragma unroll
+#pragma unroll
                     for (int k = 0; k < K - 1; ++k) {
-                        const int d = K - 1 - k;             // X[pos+1+k] is bx of the token d rows back
-                        float h = hx[K - 1 + j - d];
+                        const int d = K - 1 - k;         // X[pos+1+k] is bx of the token d rows back
+                        float h = hx[j + k];
                         if (pos < d) h = (pos >= 0 && row >= K - 1) ? s0(s_seq[row], pos + 1 + k) : 0.f;
                         conv = fmaf(wk[k], h, conv);
                     }
                     stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
                     if (a.fin != nullptr && row >= K - 1 && pos >= 0 && pos == s_len[row] - 1) {
-                        // final state X[len .. len+K-1]: bx of the last tokens, or initial-state entries
+                        // final state X[len .. len+K-1]: bx of the last tokens (rows row-K+1+e,
+                        // i.e. hx[j + e]), or initial-state entries
                         const int len = pos + 1, seq = s_seq[row];
                         uint16_t* f = a.fin + (int64_t)seq * H * K + (int64_t)ch * K;
-    #pragma unroll
+#pragma unroll
                         for (int e = 0; e < K; ++e) {
                             const int idx = len + e;
-                            f[e] = bf16_bits(idx >= K ? bxc[row + 1 + e - K] : s0(seq, idx));
+                            f[e] = bf16_bits(idx >= K ? hx[j + e] : s0(seq, idx));
                         }
                     }
                 }
@@ -420,13 +472,25 @@ int64_t fused_tiles(int64_t total_T, int H, int K) {
     return (total_T + out - 1) / out * (H / kFNC);
 }
 
+int fused_depth_multiple() { return kFBK * kFStages; }
+
+template <int K, int NK>
+static void fused_launch_main(const FusedArgs& a, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((fused_prefill_kernel<K, NK>), dim3(blocks), dim3(kFThreads), 0, s, a);
+}
+
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
     const int64_t out = fused_out_rows<K>();
     a.tiles_m = (int)((a.total_T + out - 1) / out);
     a.tiles_n = a.H / kFNC;
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
-    hipLaunchKernelGGL((fused_prefill_kernel<K>), dim3(blocks), dim3(kFThreads), 0, s, a);
+    switch (a.D) {      // straight-line reductions for the LFM2 hidden sizes
+        case 1024: fused_launch_main<K, 1024 / kFBK>(a, blocks, s); break;
+        case 1536: fused_launch_main<K, 1536 / kFBK>(a, blocks, s); break;
+        case 2048: fused_launch_main<K, 2048 / kFBK>(a, blocks, s); break;
+        default: fused_launch_main<K, 0>(a, blocks, s); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.fin == nullptr) return e;
     const int64_t chunks = (int64_t)a.H * K / 8;

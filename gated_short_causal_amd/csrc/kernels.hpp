@@ -83,6 +83,8 @@ struct FusedArgs {
 hipError_t launch_fused_prefill(const FusedArgs& a, int K, hipStream_t s);
 // Tiles of a fused launch (host-side size checks).
 int64_t fused_tiles(int64_t total_T, int H, int K);
+// D must be a positive multiple of this (the reduction's stage depth times its ring depth).
+int fused_depth_multiple();
 
 // Rows of dW/dbias partials (one per workgroup window, H*(K+1) elements each)
 // a backward launch of these sizes writes to its workspace, and the bytes of

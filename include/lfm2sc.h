@@ -252,7 +252,7 @@ const char* lfm2sc_last_error(void);
  *             installs them into the slots once every tile has read its
  *             initial states.
  * Requirements beyond the shared ones: dtype LFM2SC_BF16 (else
- * LFM2SC_ERR_UNSUPPORTED); H % 64 == 0, D % 64 == 0, 3H*D*2 < 2^31 and
+ * LFM2SC_ERR_UNSUPPORTED); H % 64 == 0, D % 128 == 0, 3H*D*2 < 2^31 and
  * 256*x_stride*2 < 2^31 (else LFM2SC_ERR_BAD_SHAPE); x_stride >= D and
  * io_stride >= 3H, multiples of 8.
  * Accuracy: B, C and xv are fp32 sums over D and are not rounded before the

@@ -199,6 +199,7 @@ def _fused(L, **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=1), UNSUP), (dict(dtype=2), UNSUP), (dict(K=5), UNSUP), (dict(bias=MIS), ALIGN),
     (dict(H=1000), SHAPE), (dict(H=72), SHAPE), (dict(D=0), SHAPE), (dict(D=1000), SHAPE), (dict(D=32), SHAPE),
+    (dict(D=192), SHAPE), (dict(D=64), SHAPE),
     (dict(H=8192, D=65536, x_stride=65536), SHAPE),
     (dict(N=-1), SHAPE), (dict(total_T=-1), SHAPE), (dict(total_T=1 << 31), SHAPE),
     (dict(x_stride=2040), SHAPE), (dict(x_stride=2052), ALIGN), (dict(x_stride=1 << 22), SHAPE),

@@ -65,8 +65,8 @@ def _check(c, y, io, pool, what):
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 def test_fused_ragged_pool_bias(K):
     lens = [37, 1, 0, 300, 5, 2]
-    _say(f"case: fused ragged K={K} lens={lens} H=128 D=192 pool+bias")
-    c = wl.fused_case(500 + K, lens, H=128, K=K, D=192, slots=9, bias=True)
+    _say(f"case: fused ragged K={K} lens={lens} H=128 D=384 pool+bias")
+    c = wl.fused_case(500 + K, lens, H=128, K=K, D=384, slots=9, bias=True)
     y, io, pool = _run(c, with_io=True)
     _check(c, y, io, pool, f"K={K}")
 
@@ -84,7 +84,7 @@ def test_fused_short_sequences_and_tail_rows():
     padded x / y / in_proj rows."""
     lens = [1, 2, 1, 0, 3, 1] * 50
     _say(f"case: fused {len(lens)} short sequences, tail rows, padded strides")
-    c = wl.fused_case(511, lens, H=64, K=3, D=64, slots=len(lens) + 4, bias=True, x_pad=8, tail_rows=7)
+    c = wl.fused_case(511, lens, H=64, K=3, D=128, slots=len(lens) + 4, bias=True, x_pad=8, tail_rows=7)
     y, io, pool = _run(c, with_io=True, y_pad=8, io_pad=16)
     _check(c, y, io, pool, "short")
 
