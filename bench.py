@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD public specification
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak, AMD public specification
 METRIC = "ShortConv GB/s and % of HBM peak; fwd+bwd ms at T=65536, H=2048, K=3"
 
 
@@ -189,6 +190,52 @@ def extra_measurements(wl_mod, steps):
     calls = [(lambda s=s, o=o: lfm2sc_verify_window(s.inp, s.w, s.pool, s.slot_idx, 8, o[1], o[0]))
              for s, o in zip(sets, outs)]
     record("verify_64x8", calls, algo_bytes_verify(64, 8, 2048, 3, 2))
+    del sets, outs, calls
+    out.update(fused_measurements(wl_mod, steps))
+    return out
+
+
+def fused_measurements(wl_mod, steps):
+    """The fused in_proj + ShortConv forward (lfm2sc_fused_prefill) at the LFM2-1.2B layer shape (D = H = 2048):
+    the training forward at T=65536 (y only, and with the in_proj output the backward takes) and the ragged
+    prefill.  Matrix-core bound: FLOPs = 2 * T * D * 3H per call against the bf16 dense peak.  `unfused_ms` is the
+    two-step path it replaces, a bf16 GEMM into in_proj (torch.matmul) then lfm2sc_prefill_ragged: context, not a
+    lower bound."""
+    import torch
+    from gated_short_causal_amd import (lfm2sc_fused_prefill, lfm2sc_fused_prefill_workspace_bytes,
+                                        lfm2sc_prefill_ragged)
+    dev = torch.device("cuda")
+    out = {}
+
+    def one(name, c, with_io, graph):
+        g = c.to(dev)
+        T, H, D = c.x.shape[0], c.H, c.D
+        N = c.cu.numel() - 1
+        y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        io = torch.empty(T, 3 * H, dtype=torch.bfloat16, device=dev) if with_io else None
+        ws = torch.empty(max(16, lfm2sc_fused_prefill_workspace_bytes(torch.bfloat16, H, c.K, N, c.pool is not None)),
+                         dtype=torch.uint8, device=dev)
+        ip = torch.empty(T, 3 * H, dtype=torch.bfloat16, device=dev)
+        fused = lambda: lfm2sc_fused_prefill(g.x, g.W_in, g.cu, g.w, y, g.pool, g.slot_idx, in_proj_out=io,
+                                             workspace=ws)
+        gemm = lambda: torch.matmul(g.x, g.W_in.t(), out=ip)
+        conv = lambda: lfm2sc_prefill_ragged(ip, g.cu, g.w, y, g.pool, g.slot_idx)
+        if graph:
+            ms = graph_time([fused], steps)
+            unf = graph_time([gemm], steps) + graph_time([conv], steps)
+        else:
+            ms = timed_loop(fused, steps, 3)
+            unf = timed_loop(gemm, steps, 3) + timed_loop(conv, steps, 3)
+        flops = 2.0 * T * D * 3 * H
+        tf = flops / ms / 1e9
+        out[name] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
+                     "unfused_ms": round(unf, 5), "T": T, "flops": flops}
+
+    one("fused_train_T65536", wl_mod.fused_train_lfm2(T=65536), False, False)
+    one("fused_train_T65536_with_in_proj", wl_mod.fused_train_lfm2(T=65536), True, False)
+    one("fused_ragged_prefill_N8", wl_mod.fused_ragged_lfm2(), False, True)
     return out
 
 
