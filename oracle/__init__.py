@@ -46,6 +46,7 @@ def _load():
         getattr(lib, name).restype = _int
     _lib = lib
     lib.oracle_in_proj.argtypes = [_i64, _int, _int, _dp, _i64, _dp, _dp]
+    lib.oracle_conv_update.argtypes = [_int, _int, _int, _int, _dp, _dp, _dp, _dp, _i64, _ip, _dp, _dp]
     return lib
 
 
@@ -184,4 +185,21 @@ def fused_prefill(x, W_in, cu, w, pool=None, slot_idx=None, bias=None):
     ip = in_proj(x, W_in)
     y, newpool = prefill(ip, cu, w, pool, slot_idx, bias)
     return y, newpool, ip
+
+
+def conv_update(bx, w, pool, slot_idx, bias=None, with_tape=True):
+    """Conv update of gated inputs bx [N, H, L] (any strides; copied dense).  Returns (out [N, H, L], tape
+    [N, L, H, K] or None, new_pool): with a tape the pool is returned unchanged, without one each named slot
+    holds the state after the L tokens."""
+    bx, w, bias = f64(bx), f64(w), f64(bias)
+    H, K = w.shape
+    N, Hb, L = bx.shape
+    assert Hb == H
+    newpool = _pool3(pool, H, K)
+    sl = i32(slot_idx)
+    out = np.full((N, H, L), np.nan)
+    tape = np.full((N, L, H, K), np.nan) if with_tape else None
+    _check(_load().oracle_conv_update(H, K, N, L, _p(bx), _p(w), _p(bias), _p(newpool), newpool.shape[0],
+                                      _p(sl, _ip), _p(tape), _p(out)), "conv_update")
+    return out, tape, newpool
 

@@ -338,3 +338,43 @@ int oracle_in_proj(int64_t rows, int D, int n_out,
     }
     return 0;
 }
+
+/* SGLang PR 31041 summary, implementation item 2 and its shortconv_target_verify
+ * excerpt: the conv update there takes Bx (already gated; the C gate is left to
+ * out_proj) as a [batch, channels, block] tensor, the slot pool, the weight and
+ * bias, and returns the conv output in the same layout, writing one conv window
+ * per draft token to the tape.  Written here on the padded history X = [state |
+ * bx], as the prefill above is. */
+int oracle_conv_update(int H, int K, int N, int L,
+                       const double* bx, const double* w, const double* bias,
+                       double* pool, int64_t num_slots, const int32_t* slot_idx,
+                       double* tape, double* out) {
+    if (H <= 0 || K <= 0 || N < 0 || L < 0) return -1;
+    if (N == 0 || L == 0) return 0;
+    if (!bx || !w || !pool || !out) return -1;
+    if (check_slots(slot_idx, N, num_slots)) return -1;
+    const int64_t HK = (int64_t)H * K;
+    int fail = 0;
+    for (int i = 0; i < N; ++i) {
+        double* S = pool + (int64_t)slot_idx[i] * HK;
+#pragma omp parallel for num_threads(g_threads) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            double* X = (double*)malloc(sizeof(double) * (size_t)(K + L));
+            if (!X) { fail = 1; continue; }
+            for (int k = 0; k < K; ++k) X[k] = S[(int64_t)h * K + k];
+            for (int s = 0; s < L; ++s) X[K + s] = bx[((int64_t)i * H + h) * L + s];
+            for (int s = 0; s < L; ++s) {
+                double conv = 0.0;
+                for (int k = 0; k < K; ++k) conv += w[(int64_t)h * K + k] * X[s + 1 + k];
+                if (bias) conv += bias[h];
+                out[((int64_t)i * H + h) * L + s] = conv;
+                if (tape)
+                    for (int k = 0; k < K; ++k) tape[(((int64_t)i * L + s) * H + h) * K + k] = X[s + 1 + k];
+            }
+            if (!tape)
+                for (int k = 0; k < K; ++k) S[(int64_t)h * K + k] = X[L + k];
+            free(X);
+        }
+    }
+    return fail ? -1 : 0;
+}

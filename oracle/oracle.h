@@ -136,6 +136,17 @@ int oracle_backward(int H, int K, int64_t total_T,
                     const double* dy, const double* d_final,
                     double* d_in, double* dW, double* dbias, double* d_init);
 
+/* Conv update on gated inputs in the [batch][channel][token] order (the layout
+ * SGLang's verify path hands its conv update, with the C gate left to
+ * out_proj): X = [state | bx of the L tokens] per channel, out[i][h][s] =
+ * bias[h] + sum_k w[h][k] X[s+1+k].  With a tape, tape[i][s] = X[s+1 .. s+K]
+ * and the pool is left as it is; with tape NULL, the slot receives
+ * X[L .. L+K-1].  bx and out dense [N][H][L], tape [N][L][H][K]. */
+int oracle_conv_update(int H, int K, int N, int L,
+                       const double* bx, const double* w, const double* bias,
+                       double* pool, int64_t num_slots, const int32_t* slot_idx,
+                       double* tape, double* out);
+
 /* in_proj = x W_in^T for the fused forward: out[t][j] = sum over d (ascending) of
  * x[t][d] * W_in[j][d], for t < rows, j < n_out; out is dense [rows][n_out]. */
 int oracle_in_proj(int64_t rows, int D, int n_out,
