@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lfm2sc_backward,
     lfm2sc_backward_workspace_bytes,
     lfm2sc_commit_window,
+    lfm2sc_conv_update,
     lfm2sc_decode_step,
     lfm2sc_fused_prefill,
     lfm2sc_fused_prefill_workspace_bytes,

@@ -32,6 +32,8 @@ SIGNATURES = {
     "lfm2sc_fused_prefill_workspace_bytes": (_size, [_int, _int, _int, _int, _int]),
     "lfm2sc_fused_prefill": (_int, [_int, _int, _int, _int, _vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64,
                                     _vp, _vp, _i64, _vp, _i64, _vp, _size, _vp]),
+    "lfm2sc_conv_update": (_int, [_int, _int, _int, _int, _int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _i64, _i64, _vp,
+                                  _vp, _vp, _i64, _i64, _i64, _vp]),
     "lfm2sc_status_string": (ctypes.c_char_p, [_int]),
     "lfm2sc_last_error": (ctypes.c_char_p, []),
     "lfm2sc_abi_version": (_int, []),

@@ -190,5 +190,23 @@ def lfm2sc_fused_prefill(x, W_in, cu_seqlens, weight, y, state_pool=None, slot_i
     return y
 
 
+def lfm2sc_conv_update(bx, weight, state_pool, slot_idx, out, windows=None, bias=None):
+    """Conv update of gated inputs bx [N, H, L] (any element strides, e.g. a transposed view of token-major rows)
+    into out [N, H, L] (any strides).  With `windows` ([N, L, H, K], contiguous) the pool is only read and every
+    step's window is written; without, each named slot advances by the L tokens."""
+    H, K = _hk(weight)
+    _i32(slot_idx, "slot_idx")
+    if bx.dim() != 3 or out.dim() != 3 or bx.shape != out.shape or bx.shape[1] != H:
+        raise ValueError(f"bx and out must both be [N, {H}, L] tensors")
+    N, _, L = bx.shape
+    if windows is not None and (not windows.is_contiguous() or windows.numel() < N * L * H * K):
+        raise ValueError(f"windows must be a contiguous [{N}, {L}, {H}, {K}] tensor")
+    _check(_lib.lib().lfm2sc_conv_update(
+        _dtype_code(weight), H, K, N, L, _ptr(bx), bx.stride(0), bx.stride(1), bx.stride(2), _ptr(weight),
+        _ptr(bias), _ptr(state_pool), state_pool.shape[0], _pool_stride(state_pool, H, K), _ptr(slot_idx),
+        _ptr(windows), _ptr(out), out.stride(0), out.stride(1), out.stride(2), _stream(bx.device)))
+    return out
+
+
 def abi_version() -> int:
     return int(_lib.lib().lfm2sc_abi_version())

@@ -3,6 +3,7 @@
 //
 // Every check here runs before the first HIP call of an entry point, so all
 // error paths can be exercised on a machine without a GPU.
+#include <type_traits>
 #include "lfm2sc.h"
 
 #include <cstdarg>
@@ -363,6 +364,47 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
     return backward_impl<float>(H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias, init_state_pool,
                                 num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state, d_in_proj, din_stride,
                                 dW, dbias, d_init_state, workspace, s);
+}
+
+int lfm2sc_conv_update(int dtype, int H, int K, int num_seqs, int L, const void* bx, int64_t bx_stride_n,
+                       int64_t bx_stride_h, int64_t bx_stride_t, const void* weight, const void* bias,
+                       void* state_pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx,
+                       void* windows, void* out, int64_t out_stride_n, int64_t out_stride_h, int64_t out_stride_t,
+                       void* stream) {
+    const char* fn = "lfm2sc_conv_update";
+    TRY(check_common(fn, dtype, H, K, bias));
+    if (num_seqs < 0 || L < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d, L=%d", fn, num_seqs, L);
+    if ((int64_t)num_seqs * L >= kMaxRows) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs*L too large", fn);
+    if (bx_stride_n < 0 || bx_stride_h < 0 || bx_stride_t < 0 || out_stride_n < 0 || out_stride_h < 0 ||
+        out_stride_t < 0)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: negative stride", fn);
+    if (num_seqs == 0 || L == 0) return ok();
+    const uintptr_t esz = dtype == LFM2SC_BF16 ? 2 : 4;
+    TRY(check_ptr(fn, "bx", bx, esz));
+    TRY(check_ptr(fn, "out", out, esz));
+    TRY(check_ptr(fn, "weight", weight, 16));
+    TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
+    if (windows != nullptr && !aligned(windows, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: windows is not 16-byte aligned", fn);
+    const bool vec = bx_stride_h == 1 && out_stride_h == 1 && bx_stride_n % 8 == 0 && bx_stride_t % 8 == 0 &&
+                     out_stride_n % 8 == 0 && out_stride_t % 8 == 0 && aligned(bx, 16) && aligned(out, 16);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TRY(device_check(fn, s, slot_idx, num_seqs, num_slots, nullptr, 0, nullptr, 0));
+    auto fill = [&](auto* tag) {
+        using E = std::remove_pointer_t<decltype(tag)>;
+        ConvUpdateArgs<E> a;
+        a.bx = static_cast<const E*>(bx); a.bx_sn = bx_stride_n; a.bx_sh = bx_stride_h; a.bx_st = bx_stride_t;
+        a.N = num_seqs; a.L = L;
+        a.w = static_cast<const E*>(weight); a.bias = static_cast<const E*>(bias);
+        a.pool = static_cast<E*>(state_pool); a.num_slots = num_slots; a.slot_stride = slot_stride;
+        a.slot_idx = slot_idx;
+        a.win = static_cast<E*>(windows);
+        a.out = static_cast<E*>(out); a.out_sn = out_stride_n; a.out_sh = out_stride_h; a.out_st = out_stride_t;
+        a.H = H;
+        return launched(fn, launch_conv_update<E>(a, K, vec, s));
+    };
+    if (dtype == LFM2SC_BF16) return fill(static_cast<uint16_t*>(nullptr));
+    return fill(static_cast<float*>(nullptr));
 }
 
 size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seqs, int with_pool) {

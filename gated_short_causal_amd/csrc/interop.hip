@@ -1,0 +1,126 @@
+// interop.hip -- conv update on gated inputs in the [batch][channel][token]
+// order, with arbitrary element strides (the layout-interop entry point).
+//
+// SGLang PR 31041 summary, implementation item 2 and its
+// shortconv_target_verify excerpt: that engine's verify path gates B and xv
+// itself, hands its conv update Bx as a [batch, channels, block] tensor (a
+// transposed view of token-major rows), takes the conv output back in the same
+// layout and leaves the C gate to out_proj; one conv window per draft token
+// goes to the tape.  This kernel serves that call directly: per sequence, X =
+// [slot state | bx of the L tokens] per channel, out = bias + sum_k w[k] X[s+1+k];
+// with a tape the pool is only read, without one the slot advances by the L
+// tokens (a multi-token decode step).
+//
+// One wave per (sequence, 512 channels), a lane owning 8 channels, as in the
+// verify kernel; up to 8 tokens' inputs are loaded before any is used.  When
+// the channel stride is 1 and the rows are 16-byte aligned (the transposed
+// view of token-major memory), bx and out move as 16-byte vectors; any other
+// strides (e.g. a dense [N][H][L] tensor) take per-element accesses.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lfm2sc {
+
+template <typename E> __device__ __forceinline__ float ld1(const E* p);
+template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <typename E> __device__ __forceinline__ void st1(E* p, float v);
+template <> __device__ __forceinline__ void st1<uint16_t>(uint16_t* p, float v) {
+    *p = (uint16_t)(Elem<uint16_t>::pack2(v, 0.f) & 0xffffu);
+}
+template <> __device__ __forceinline__ void st1<float>(float* p, float v) { *p = v; }
+
+template <typename E, int K, bool VEC>
+__global__ __launch_bounds__(kSmallBlock) void conv_update_kernel(const ConvUpdateArgs<E> a) {
+    constexpr int U = 8;
+    const int i = blockIdx.x;
+    const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
+    if (ch0 >= a.H) return;
+    const int64_t slot = a.slot_idx[i];
+    const bool ok = slot_ok(slot, a.num_slots);
+    float wf[kChPerLane][K];
+    load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float bv[kChPerLane] = {};
+    if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
+    E* sp = ok ? a.pool + slot * a.slot_stride + (int64_t)ch0 * K : nullptr;
+    float s[kChPerLane][K];
+    if (ok) {
+        load_block<E, K>(sp, s);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int k = 0; k < K; ++k) s[c][k] = 0.f;
+    }
+    const E* bxi = a.bx + (int64_t)i * a.bx_sn + (int64_t)ch0 * a.bx_sh;
+    E* oi = a.out + (int64_t)i * a.out_sn + (int64_t)ch0 * a.out_sh;
+    for (int t0 = 0; t0 < a.L; t0 += U) {
+        const int n = a.L - t0 < U ? a.L - t0 : U;
+        float x[U][kChPerLane];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u < n) {
+                const E* p = bxi + (int64_t)(t0 + u) * a.bx_st;
+                if constexpr (VEC) {
+                    load_f32x8<E>(p, x[u]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) x[u][c] = ld1<E>(p + (int64_t)c * a.bx_sh);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (u < n) {
+                float y[kChPerLane];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+#pragma unroll
+                    for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
+                    s[c][K - 1] = x[u][c];
+                    float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
+#pragma unroll
+                    for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
+                    y[c] = conv;
+                }
+                E* q = oi + (int64_t)(t0 + u) * a.out_st;
+                if constexpr (VEC) {
+                    store_f32x8<E>(q, y);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
+                }
+                if (a.win != nullptr)
+                    store_block<E, K>(a.win + (((int64_t)i * a.L + t0 + u) * a.H + ch0) * K, s);
+            }
+        }
+    }
+    if (a.win == nullptr && ok) store_block<E, K>(sp, s);
+}
+
+template <typename E, int K>
+static hipError_t conv_update_k(const ConvUpdateArgs<E>& a, bool vec, hipStream_t st) {
+    const int lanes = a.H / kChPerLane;
+    const dim3 grid(a.N, (lanes + kSmallBlock - 1) / kSmallBlock);
+    if (vec)
+        hipLaunchKernelGGL((conv_update_kernel<E, K, true>), grid, dim3(kSmallBlock), 0, st, a);
+    else
+        hipLaunchKernelGGL((conv_update_kernel<E, K, false>), grid, dim3(kSmallBlock), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, bool vec, hipStream_t s) {
+    switch (K) {
+        case 1: return conv_update_k<E, 1>(a, vec, s);
+        case 2: return conv_update_k<E, 2>(a, vec, s);
+        case 3: return conv_update_k<E, 3>(a, vec, s);
+        case 4: return conv_update_k<E, 4>(a, vec, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template hipError_t launch_conv_update<uint16_t>(const ConvUpdateArgs<uint16_t>&, int, bool, hipStream_t);
+template hipError_t launch_conv_update<float>(const ConvUpdateArgs<float>&, int, bool, hipStream_t);
+
+}  // namespace lfm2sc

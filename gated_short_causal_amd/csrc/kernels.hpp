@@ -64,6 +64,21 @@ struct BackwardArgs {
     int ntiles;
 };
 
+// Conv update of gated inputs bx[n][h][t] (element strides sn, sh, st) into
+// out[n][h][t]; tape win [N][L][H][K] or nullptr (then the slot advances).
+template <typename E>
+struct ConvUpdateArgs {
+    const E* bx; int64_t bx_sn, bx_sh, bx_st;
+    int N, L;
+    const E* w; const E* bias;
+    E* pool; int64_t num_slots; int64_t slot_stride; const int32_t* slot_idx;
+    E* win;
+    E* out; int64_t out_sn, out_sh, out_st;
+    int H;
+};
+// vec: channel stride 1 and 16-byte aligned rows for both bx and out.
+template <typename E> hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, bool vec, hipStream_t s);
+
 // Fused in_proj GEMM + ShortConv forward (bf16 only).  x [total_T][x_stride]
 // (D used), W [3H][D]; y [total_T][y_stride]; io: optional in_proj output
 // [total_T][io_stride] (B | C | xv, bf16); fin: [N][H][K] staging for the final

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LFM2SC_ABI_VERSION 3
+#define LFM2SC_ABI_VERSION 4
 
 enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
 
@@ -271,6 +271,41 @@ int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
 
 /* Workspace bytes of lfm2sc_fused_prefill (0 when with_pool is 0). */
 size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seqs, int with_pool);
+
+/*
+ * Conv update of gated inputs in [batch][channel][token] order with arbitrary
+ * element strides: the layout-interop form of the verify / multi-token decode
+ * step, for engines that gate B and xv themselves and keep the C gate for
+ * out_proj.
+ *
+ * Passage: SGLang PR 31041 summary, implementation item 2 and its
+ * shortconv_target_verify excerpt (the conv update takes Bx as a [batch,
+ * channels, block] tensor -- there a transposed view of token-major rows --
+ * with the slot pool, weight and bias, returns the conv output in the same
+ * layout and writes one window per draft token to the tape).
+ *
+ * bx     element (n, h, t) at bx[n*bx_stride_n + h*bx_stride_h + t*bx_stride_t],
+ *        n < num_seqs, h < H, t < L: the gated input B*xv of token t.
+ * out    element (n, h, t) at out[n*out_stride_n + h*out_stride_h + t*out_stride_t]:
+ *        bias[h] + sum_k weight[h][k] * X[t+1+k] with X = [slot state | bx of
+ *        tokens 0..L-1] (no C gate).  out must not overlap bx.
+ * state_pool, num_slots, slot_stride, slot_idx: as in lfm2sc_verify_window.
+ * windows [num_seqs][L][H][K] (16-byte aligned) or NULL.  Given: windows[n][t]
+ *        receives X[t+1 .. t+K] (the state after token t) and the pool is only
+ *        read; commit with lfm2sc_commit_window.  NULL: each named slot
+ *        receives X[L .. L+K-1] in place (the state after the L tokens).
+ * Strides are in elements and must be >= 0; bx and out need only element
+ * alignment.  When bx_stride_h == out_stride_h == 1, the other strides are
+ * multiples of 8 and bx, out are 16-byte aligned, the kernel moves 16-byte
+ * vectors; otherwise it accesses single elements (slower, same results).
+ */
+int lfm2sc_conv_update(int dtype, int H, int K, int num_seqs, int L,
+                       const void* bx, int64_t bx_stride_n, int64_t bx_stride_h, int64_t bx_stride_t,
+                       const void* weight, const void* bias,
+                       void* state_pool, int64_t num_slots, int64_t slot_stride,
+                       const int32_t* slot_idx, void* windows,
+                       void* out, int64_t out_stride_n, int64_t out_stride_h, int64_t out_stride_t,
+                       void* stream);
 
 /* LFM2SC_ABI_VERSION of the loaded library. */
 int lfm2sc_abi_version(void);

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
     for n in names:
         assert hasattr(L, n), n
@@ -228,4 +228,32 @@ def test_fused_workspace_bytes(L):
     assert L.lfm2sc_fused_prefill_workspace_bytes(0, 64, 1, 1, 1) == 256
     assert L.lfm2sc_fused_prefill_workspace_bytes(1, 2048, 3, 8, 1) == 0     # fp32 unsupported
     assert L.lfm2sc_fused_prefill_workspace_bytes(0, 72, 3, 8, 1) == 0       # H % 64 != 0
+
+
+def _cu(lib, **kw):
+    a = dict(dtype=0, H=2048, K=3, N=64, L=8, bx=P, bsn=8 * 2048, bsh=1, bst=2048, w=P, bias=None, pool=P,
+             num_slots=256, slot_stride=6144, slot_idx=P, win=None, out=P, osn=8 * 2048, osh=1, ost=2048,
+             stream=None)
+    a.update(kw)
+    return lib.lfm2sc_conv_update(a["dtype"], a["H"], a["K"], a["N"], a["L"], a["bx"], a["bsn"], a["bsh"], a["bst"],
+                                  a["w"], a["bias"], a["pool"], a["num_slots"], a["slot_stride"], a["slot_idx"],
+                                  a["win"], a["out"], a["osn"], a["osh"], a["ost"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), UNSUP), (dict(K=5), UNSUP), (dict(H=12), SHAPE), (dict(bias=MIS), ALIGN),
+    (dict(N=-1), SHAPE), (dict(L=-1), SHAPE), (dict(N=1 << 20, L=1 << 12), SHAPE),
+    (dict(bsn=-1), SHAPE), (dict(bsh=-8), SHAPE), (dict(ost=-1), SHAPE),
+    (dict(bx=None), NULLP), (dict(out=None), NULLP), (dict(bx=P + 1), ALIGN), (dict(dtype=1, out=P + 2), ALIGN),
+    (dict(w=None), NULLP), (dict(pool=None), NULLP), (dict(slot_idx=None), NULLP),
+    (dict(slot_stride=6000), SHAPE), (dict(win=P + 8), ALIGN),
+])
+def test_conv_update_rejects(L, kw, code):
+    assert _cu(L, **kw) == code
+    assert L.lfm2sc_last_error().decode().startswith("lfm2sc_conv_update")
+
+
+def test_conv_update_no_work_is_ok(L):
+    assert _cu(L, N=0, bx=None, out=None, pool=None, slot_idx=None) == OK
+    assert _cu(L, L=0, bx=None, out=None, pool=None, slot_idx=None) == OK
 
