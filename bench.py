@@ -54,6 +54,11 @@ def algo_bytes_verify(N, L, H, K, e):
     return N * L * (3 * H * e + H * e + H * K * e) + N * H * K * e + H * K * e + 4 * N
 
 
+def algo_bytes_conv_update(N, L, H, K, e):
+    """Read bx and write out (H per token), write the tape (H*K per token), read each state; weight, slot ids."""
+    return N * L * (2 * H * e + H * K * e) + N * H * K * e + H * K * e + 4 * N
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in ("bwd.hip", "common.hpp", "kernels.hpp"):
@@ -191,7 +196,57 @@ def extra_measurements(wl_mod, steps):
              for s, o in zip(sets, outs)]
     record("verify_64x8", calls, algo_bytes_verify(64, 8, 2048, 3, 2))
     del sets, outs, calls
+    # conv update of gated inputs at the verify shape, in the transposed-view layout of token-major rows
+    # (vector path) and as a dense [N][H][L] tensor (per-element path): bx, out, tape and the read of the state
+    from gated_short_causal_amd import lfm2sc_conv_update
+    for kind in ("view", "dense"):
+        sets = [wl_mod.verify_lfm2(seed=450 + i).to(dev) for i in range(48)]
+        bxs, outs, tapes = [], [], []
+        for st in sets:
+            rows = st.inp[:, :2048]                                   # stands in for gated B*xv rows
+            if kind == "view":
+                bxs.append(rows.contiguous().view(64, 8, 2048).transpose(1, 2))
+                outs.append(torch.empty(64, 8, 2048, dtype=torch.bfloat16, device=dev).transpose(1, 2))
+            else:
+                bxs.append(rows.view(64, 8, 2048).transpose(1, 2).contiguous())
+                outs.append(torch.empty(64, 2048, 8, dtype=torch.bfloat16, device=dev))
+            tapes.append(torch.empty(64, 8, 2048, 3, dtype=torch.bfloat16, device=dev))
+        calls = [(lambda st=st, b=b, o=o, t=t: lfm2sc_conv_update(b, st.w, st.pool, st.slot_idx, o, windows=t))
+                 for st, b, o, t in zip(sets, bxs, outs, tapes)]
+        record(f"conv_update_64x8_{kind}", calls, algo_bytes_conv_update(64, 8, 2048, 3, 2))
+        del sets, bxs, outs, tapes, calls
     out.update(fused_measurements(wl_mod, steps))
+    out.update(shape_measurements(wl_mod, steps))
+    return out
+
+
+def shape_measurements(wl_mod, steps):
+    """The training step (prefill forward + backward, T=65536, one sequence) at other channel counts and tap
+    counts, and with fp32 I/O: GB/s of the step's algorithmic bytes and % of the HBM peak."""
+    import torch
+    from gated_short_causal_amd import lfm2sc_backward, lfm2sc_backward_workspace_bytes, lfm2sc_prefill_ragged
+    dev = torch.device("cuda")
+    out = {}
+    for H, K, dt in ((1024, 3, torch.bfloat16), (1536, 3, torch.bfloat16), (2048, 2, torch.bfloat16),
+                     (2048, 4, torch.bfloat16), (2048, 3, torch.float32)):
+        T = 65536
+        e = 2 if dt == torch.bfloat16 else 4
+        c = wl_mod.train_lfm2(seed=5, T=T, H=H, K=K, dtype=dt).to(dev)
+        y = torch.empty(T, H, dtype=dt, device=dev)
+        d_in = torch.empty(T, 3 * H, dtype=dt, device=dev)
+        dW = torch.empty(H, K, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, lfm2sc_backward_workspace_bytes(dt, H, K, T, 1)), dtype=torch.uint8, device=dev)
+
+        def step():
+            lfm2sc_prefill_ragged(c.inp, c.cu, c.w, y)
+            lfm2sc_backward(c.inp, c.cu, c.w, c.dy, d_in, dW, ws)
+
+        ms = timed_loop(step, steps, 3)
+        nbytes = algo_bytes_fwd(T, H, K, e) + algo_bytes_bwd(T, H, K, e)
+        name = f"train_T65536_H{H}_K{K}_{'bf16' if e == 2 else 'fp32'}"
+        out[name] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
+                     "pct_of_hbm_peak": round(100 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 1), "bytes": int(nbytes)}
+        del c, y, d_in, dW, ws
     return out
 
 

@@ -295,8 +295,14 @@ struct WgLayout {
     static int groups(int H) { return (H + kChPerBlock - 1) / kChPerBlock; }
 };
 
+// Window slots are counted per XCD: the launch pads the window count to a
+// multiple of 8 and each XCD runs `groups` workgroups for each of its windows,
+// so a chip-wide count (e.g. 85 windows x 3 groups = 255 <= 256) can still put
+// 33 workgroups on an XCD of 32 CUs and push one into a second round.
 inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, int tw) {
-    const int64_t slots = (int64_t)resident * LFM2SC_ROUNDS / (groups > 0 ? groups : 1);
+    const int64_t g = groups > 0 ? groups : 1;
+    const int64_t per_xcd = (int64_t)resident * LFM2SC_ROUNDS / kXcds / g;
+    const int64_t slots = (per_xcd > 0 ? per_xcd : 1) * kXcds;
     const int64_t free = slots - N;
     const int64_t denom = (int64_t)tw * (free >= 1 ? free : (slots > 0 ? slots : 1));
     int64_t sub = (total_T + denom - 1) / denom;

@@ -376,3 +376,26 @@ def test_chunked_training_on_gpu():
     assert_close(torch.cat([d1, d2]), d_ref, c.dtype, "chunked d_in")
     assert_close(dW1 + dW2, dW_ref, c.dtype, "chunked dW")
     assert_close(dS0, di_ref, c.dtype, "chunked d_init")
+
+
+@pytest.mark.parametrize("H,K,dtype", [(1024, 2, torch.bfloat16), (1536, 4, torch.bfloat16), (1536, 3, torch.float32)])
+def test_other_sizes_training_step(H, K, dtype):
+    """Training step (prefill forward + backward) at other channel and tap counts, two sequences, full parity."""
+    _say(f"case: training step H={H} K={K} {dtype}")
+    c = wl.random_case(120 + K, [1700, 301], H=H, K=K, dtype=dtype, slots=3, with_dy=True)
+    g = c.to(DEV)
+    pool0 = g.pool.clone()
+    T = 2001
+    y = _nan((T, H), dtype)
+    lfm2sc_prefill_ragged(g.inp, g.cu, g.w, y, g.pool, g.slot_idx)
+    d_in = _nan((T, 3 * H), dtype)
+    dW = _nan((H, K), torch.float32)
+    ws = torch.empty(lfm2sc_backward_workspace_bytes(dtype, H, K, T, 2), dtype=torch.uint8, device=DEV)
+    lfm2sc_backward(g.inp, g.cu, g.w, g.dy, d_in, dW, ws, pool0, g.slot_idx)
+    torch.cuda.synchronize()
+    y_ref, p_ref = oracle.prefill(c.inp, c.cu, c.w, c.pool, c.slot_idx)
+    d_ref, dW_ref = oracle.backward(c.inp, c.cu, c.w, c.dy, c.pool, c.slot_idx)
+    assert_close(y, y_ref, dtype, "y")
+    assert_bits(g.pool, rounded(p_ref, dtype), "states")
+    assert_close(d_in, d_ref, dtype, "d_in")
+    assert_close(dW, dW_ref, dtype, "dW")
