@@ -15,6 +15,9 @@
 #include <stdint.h>
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef LFM2SC_VERIFY_U
+#define LFM2SC_VERIFY_U 1      // draft steps per verify wave (the steps of a sequence are split over waves)
+#endif
 #ifndef LFM2SC_ROUNDS
 #define LFM2SC_ROUNDS 1        // ragged grids are sized to this many full rounds of resident workgroups
 #endif

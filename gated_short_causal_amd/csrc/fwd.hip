@@ -252,61 +252,105 @@ __global__ __launch_bounds__(kSmallBlock) void decode_kernel(const DecodeArgs<E>
 
 // ------------------------------------------------------------------ verify
 // L draft tokens per sequence from the slot state (read only); after each
-// token the lane's 8 x K window goes to the tape windows[i][s].
+// token the lane's 8 x K window goes to the tape windows[i][s].  The steps are
+// split over blockIdx.z in blocks of U: the window entering a block's first
+// step s0 is X[s0 .. s0+K-1] of X = [state | bx of the draft tokens] (entry
+// s0 is shifted out before use), i.e. state entries for the first K-1 steps
+// and otherwise bx of the K-1 tokens before s0, recomputed from their B and
+// xv rows.  Only blocks that start inside the first K-1 steps read the slot,
+// so most waves skip the slot -> state round trip, and more waves share the
+// work of one sequence.
 template <typename E, int K, int U>
 __global__ __launch_bounds__(kSmallBlock) void verify_kernel(const VerifyArgs<E> a) {
+    constexpr int KH = K > 1 ? K - 1 : 1;
     const int i = blockIdx.x;
     const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
     if (ch0 >= a.H) return;
+    const int s0 = blockIdx.z * U;
+    const int n = a.L - s0 < U ? a.L - s0 : U;
+    if (n <= 0) return;
     const int H = a.H;
     const int64_t HK = (int64_t)H * K;
-    const int64_t slot = a.slot_idx[i];
+    const E* base = a.in + (int64_t)i * a.L * a.in_stride + ch0;
+    // Loads first, all independent: the K-1 history rows (B, xv), the block's rows (B, C, xv), the state.
+    Raw8<E> hb[KH], hx[KH];
+#pragma unroll
+    for (int k = 1; k < K; ++k) {
+        const int t = s0 + k - K;                      // token whose bx is window entry k
+        if (t >= 0) {
+            const E* row = base + (int64_t)t * a.in_stride;
+            hb[k - 1] = ld8<E>(row); hx[k - 1] = ld8<E>(row + 2 * H);
+        }
+    }
+    Raw8<E> rb[U], rc[U], rx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u < n) {
+            const E* row = base + (int64_t)(s0 + u) * a.in_stride;
+            rb[u] = ld8<E>(row); rc[u] = ld8<E>(row + H); rx[u] = ld8<E>(row + 2 * H);
+        }
+    }
+    float st[kChPerLane][K];
+    const bool need_state = s0 + 1 < K;
+    if (need_state) {
+        const int64_t slot = a.slot_idx[i];
+        if (slot_ok(slot, a.num_slots)) {
+            load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, st);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int k = 0; k < K; ++k) st[c][k] = 0.f;
+        }
+    }
     float wf[kChPerLane][K];
     load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
     float bv[kChPerLane] = {};
     if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
+
+    // window entering step s0: s[c][k] = X[s0 + k] for k >= 1
     float s[kChPerLane][K];
-    if (slot_ok(slot, a.num_slots)) {
-        load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, s);
-    } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
+    for (int k = 0; k < K; ++k) {
+        const int idx = s0 + k;                        // index into X
+        if (k == 0) {
 #pragma unroll
-            for (int k = 0; k < K; ++k) s[c][k] = 0.f;
+            for (int c = 0; c < 8; ++c) s[c][0] = 0.f; // shifted out before it is used
+        } else if (idx < K) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                float v = 0.f;
+#pragma unroll
+                for (int m = 1; m < K; ++m) v = (m == idx) ? st[c][m] : v;
+                s[c][k] = v;
+            }
+        } else {
+            float b[8], x[8];
+            to_f32(hb[k - 1], b); to_f32(hx[k - 1], x);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s[c][k] = b[c] * x[c];
+        }
     }
-    const E* base = a.in + (int64_t)i * a.L * a.in_stride + ch0;
     E* ybase = a.y + (int64_t)i * a.L * a.y_stride + ch0;
     E* tbase = a.win + (int64_t)i * a.L * HK + (int64_t)ch0 * K;
-    int st = 0;
-    auto step = [&](const Raw8<E>& rb, const Raw8<E>& rc, const Raw8<E>& rx, int s_) {
-        float b[8], c8[8], x[8], yv[8];
-        to_f32(rb, b); to_f32(rc, c8); to_f32(rx, x);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+    for (int u = 0; u < U; ++u) {
+        if (u < n) {
+            float b[8], c8[8], x[8], yv[8];
+            to_f32(rb[u], b); to_f32(rc[u], c8); to_f32(rx[u], x);
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
-            s[c][K - 1] = b[c] * x[c];
-            float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
+            for (int c = 0; c < 8; ++c) {
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
-            yv[c] = c8[c] * conv;
+                for (int k = 0; k < K - 1; ++k) s[c][k] = s[c][k + 1];
+                s[c][K - 1] = b[c] * x[c];
+                float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
+                yv[c] = c8[c] * conv;
+            }
+            store_f32x8<E>(ybase + (int64_t)(s0 + u) * a.y_stride, yv);
+            store_block<E, K>(tbase + (int64_t)(s0 + u) * HK, s);
         }
-        store_f32x8<E>(ybase + (int64_t)s_ * a.y_stride, yv);
-        store_block<E, K>(tbase + (int64_t)s_ * HK, s);
-    };
-    for (; st + U <= a.L; st += U) {
-        Raw8<E> rb[U], rc[U], rx[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const E* row = base + (int64_t)(st + u) * a.in_stride;
-            rb[u] = ld8<E>(row); rc[u] = ld8<E>(row + H); rx[u] = ld8<E>(row + 2 * H);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) step(rb[u], rc[u], rx[u], st + u);
-    }
-    for (; st < a.L; ++st) {
-        const E* row = base + (int64_t)st * a.in_stride;
-        step(ld8<E>(row), ld8<E>(row + H), ld8<E>(row + 2 * H), st);
     }
 }
 
@@ -377,7 +421,9 @@ hipError_t launch_decode(const DecodeArgs<E>& a, int K, hipStream_t s) {
 template <typename E, int K>
 static hipError_t verify_k(const VerifyArgs<E>& a, hipStream_t s) {
     const int lanes = a.H / kChPerLane;
-    hipLaunchKernelGGL((verify_kernel<E, K, 8>), dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock), dim3(kSmallBlock),
+    constexpr int U = LFM2SC_VERIFY_U;
+    hipLaunchKernelGGL((verify_kernel<E, K, U>),
+                       dim3(a.N, (lanes + kSmallBlock - 1) / kSmallBlock, (a.L + U - 1) / U), dim3(kSmallBlock),
                        0, s, a);
     return hipGetLastError();
 }
