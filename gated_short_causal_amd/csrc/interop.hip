@@ -9,7 +9,9 @@
 // goes to the tape.  This kernel serves that call directly: per sequence, X =
 // [slot state | bx of the L tokens] per channel, out = bias + sum_k w[k] X[s+1+k];
 // with a tape the pool is only read, without one the slot advances by the L
-// tokens (a multi-token decode step).
+// tokens (a multi-token decode step).  With a tape the steps run one per wave
+// (conv_update_step_kernel); in place, one wave walks a sequence's steps, since
+// it both reads and writes the slot.
 //
 // One wave per (sequence, 512 channels), a lane owning 8 channels, as in the
 // verify kernel; up to 8 tokens' inputs are loaded before any is used.  When
@@ -98,10 +100,93 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_kernel(const ConvUpda
     if (a.win == nullptr && ok) store_block<E, K>(sp, s);
 }
 
+// Tape mode: the pool is only read, so the L steps of a sequence can be split
+// over waves, one step each (blockIdx.z): the window entering step t0 is
+// X[t0 .. t0+K-1] (entry t0 shifted out before use), built from bx of the K-1
+// previous tokens or, for the first K-1 steps, from the slot state; only those
+// waves read the slot.
+template <typename E, int K, bool VEC>
+__global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const ConvUpdateArgs<E> a) {
+    constexpr int KH = K > 1 ? K - 1 : 1;
+    const int i = blockIdx.x;
+    const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
+    if (ch0 >= a.H) return;
+    const int t0 = blockIdx.z;
+    const E* bxi = a.bx + (int64_t)i * a.bx_sn + (int64_t)ch0 * a.bx_sh;
+    auto load_bx = [&](int t, float* x) {
+        const E* p = bxi + (int64_t)t * a.bx_st;
+        if constexpr (VEC) {
+            load_f32x8<E>(p, x);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = ld1<E>(p + (int64_t)c * a.bx_sh);
+        }
+    };
+    float hist[KH][kChPerLane], x[kChPerLane];
+#pragma unroll
+    for (int k = 1; k < K; ++k)
+        if (t0 + k - K >= 0) load_bx(t0 + k - K, hist[k - 1]);
+    load_bx(t0, x);
+    float st[kChPerLane][K];
+    if (t0 + 1 < K) {
+        const int64_t slot = a.slot_idx[i];
+        if (slot_ok(slot, a.num_slots)) {
+            load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, st);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int k = 0; k < K; ++k) st[c][k] = 0.f;
+        }
+    }
+    float wf[kChPerLane][K];
+    load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
+    float bv[kChPerLane] = {};
+    if (a.bias != nullptr) load_f32x8<E>(a.bias + ch0, bv);
+    // window after step t0: X[t0+1 .. t0+K]
+    float s[kChPerLane][K], y[kChPerLane];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+        for (int k = 1; k < K; ++k) {
+            const int idx = t0 + k;
+            float v = 0.f;
+            if (idx < K) {
+#pragma unroll
+                for (int m = 1; m < K; ++m) v = (m == idx) ? st[c][m] : v;
+            } else {
+                v = hist[k - 1][c];
+            }
+            s[c][k - 1] = v;
+        }
+        s[c][K - 1] = x[c];
+        float conv = fmaf(wf[c][K - 1], s[c][K - 1], bv[c]);
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
+        y[c] = conv;
+    }
+    E* q = a.out + (int64_t)i * a.out_sn + (int64_t)ch0 * a.out_sh + (int64_t)t0 * a.out_st;
+    if constexpr (VEC) {
+        store_f32x8<E>(q, y);
+    } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
+    }
+    store_block<E, K>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
+}
+
 template <typename E, int K>
 static hipError_t conv_update_k(const ConvUpdateArgs<E>& a, bool vec, hipStream_t st) {
     const int lanes = a.H / kChPerLane;
     const dim3 grid(a.N, (lanes + kSmallBlock - 1) / kSmallBlock);
+    if (a.win != nullptr) {
+        const dim3 g3(a.N, grid.y, a.L);
+        if (vec)
+            hipLaunchKernelGGL((conv_update_step_kernel<E, K, true>), g3, dim3(kSmallBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((conv_update_step_kernel<E, K, false>), g3, dim3(kSmallBlock), 0, st, a);
+        return hipGetLastError();
+    }
     if (vec)
         hipLaunchKernelGGL((conv_update_kernel<E, K, true>), grid, dim3(kSmallBlock), 0, st, a);
     else
