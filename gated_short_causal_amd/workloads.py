@@ -198,3 +198,47 @@ def fused_ragged_lfm2(seed: int = 7, N: int = 8, lo: int = 64, hi: int = 2048, H
     g = torch.Generator().manual_seed(seed)
     lens = torch.randint(lo, hi + 1, (N,), generator=g).tolist()
     return fused_case(seed + 1000, lens, H, K, D, slots=N)
+
+
+def _normal_on(g, shape, dtype, device):
+    return torch.randn(shape, generator=g, dtype=torch.float32, device=device).to(dtype)
+
+
+def large_train_on(device, seed: int, lens, H: int = H_LFM2, K: int = K_LFM2, slots: int = 0,
+                   dtype=torch.bfloat16) -> Workload:
+    """Maximum-size cases drawn directly on `device` (a generator of that device, same recipe: N(0,1) inputs,
+    dy and pool, U(-0.5,0.5) weight), so that multi-GB inputs need no host copy."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    lens = torch.as_tensor(list(lens), dtype=torch.int64)
+    N = lens.numel()
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    total = int(cu[-1])
+    inp = _normal_on(g, (total, 3 * H), dtype, device)
+    w = (torch.rand((H, K), generator=g, dtype=torch.float32, device=device) - 0.5).to(dtype)
+    dy = _normal_on(g, (total, H), dtype, device)
+    pool = slot_idx = None
+    if slots:
+        pool = _normal_on(g, (slots, H, K), dtype, device)
+        slot_idx = torch.randperm(slots, generator=g, device=device)[:N].to(torch.int32)
+    return Workload("large_train", dtype, H, K, inp, w, cu=cu.to(device), pool=pool, slot_idx=slot_idx, dy=dy)
+
+
+def large_fused_on(device, seed: int, lens, H: int = H_LFM2, K: int = K_LFM2, D: int = H_LFM2,
+                   slots: int = 0) -> FusedWorkload:
+    """Maximum-size fused-forward case drawn on `device`: x ~ N(0,1), W_in ~ N(0, 1/D), w ~ U(-0.5,0.5)."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    lens = torch.as_tensor(list(lens), dtype=torch.int64)
+    N = lens.numel()
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    total = int(cu[-1])
+    dt = torch.bfloat16
+    x = _normal_on(g, (total, D), dt, device)
+    W_in = (torch.randn((3 * H, D), generator=g, dtype=torch.float32, device=device) * D ** -0.5).to(dt)
+    w = (torch.rand((H, K), generator=g, dtype=torch.float32, device=device) - 0.5).to(dt)
+    pool = slot_idx = None
+    if slots:
+        pool = _normal_on(g, (slots, H, K), dt, device)
+        slot_idx = torch.randperm(slots, generator=g, device=device)[:N].to(torch.int32)
+    return FusedWorkload("large_fused", H, K, D, x, W_in, w, cu.to(device), pool=pool, slot_idx=slot_idx)
