@@ -17,7 +17,9 @@
 // and xv of the same channel and rows in its accumulators.  Consecutive tiles
 // overlap by K-1 rows: a tile outputs rows K-1 .. 255 of the rows it computes,
 // so the conv history of every output row is inside the tile (0.8% extra MFMA
-// work at K = 3).
+// work at K = 3).  When H % 128 == 0 and D is one of the LFM2 hidden sizes a
+// wide variant (fused_wide_kernel) covers 128 channels with 8 waves instead,
+// the same 128 x 32 block per wave, which halves the x rows fetched per FLOP.
 //
 // Reduction.  Stages of kFBK = 32 along D.  The x rows and W_in rows of a stage
 // go from global memory straight into one slot of a 4-deep LDS ring (buffer
@@ -453,6 +455,297 @@ void fused_prefill_kernel(const FusedArgs a) {
     flush_rows(a.y, a.y_stride, true);
 }
 
+// ---------------------------------------------------------------- wide tiles
+// The tile above fetches 28 KiB per stage for its MFMA work; on MI355X its
+// loop waits on the vector-memory data path (L2 -> CU), which hardware
+// counters show busy ~80% of the time.  Wide tiles cover 128 channels with 8
+// waves (two per SIMD), each wave still 128 rows x 32 channels, so a stage
+// moves 40 KiB for twice the MFMA work (1.4x less data per FLOP).  Used when
+// H % 128 == 0 and D is one of the unrolled hidden sizes.
+constexpr int kWNC = 128;                          // channels per wide tile
+constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
+constexpr int kWStages = 3;                        // ring depth: 2 stages in flight ahead of the one in use
+constexpr int kWStageA = kFBM * kFRowBytes;        // 16 KiB of x rows
+constexpr int kWStageB = 3 * kWNC * kFRowBytes;    // 24 KiB of W_in rows
+constexpr int kWDmaA = kFBM / 16 / 8;              // 2 blocks of 16 x rows per wave
+constexpr int kWDmaB = 3 * kWNC / 16 / 8;          // 3 blocks of 16 W_in rows per wave
+constexpr int kWVm = kWDmaA + kWDmaB;
+constexpr int kWRegion = 128 * 32 * 2;             // one wave's bf16 output block: 128 rows x 32 channels
+
+template <int KT, int NK, typename F>
+__device__ __forceinline__ void unroll_stages(F& f) {
+    if constexpr (KT < NK) {
+        f(IC<KT>{});
+        unroll_stages<KT + 1, NK>(f);
+    }
+}
+
+template <int K, int NK>
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fused_wide_kernel(const FusedArgs a) {
+    static_assert(NK >= 2, "at least two stages");
+    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA];
+    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB];
+    __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
+    __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ float s_edge[4][32][4];           // bx of rows 125..127 per channel group (the second half's history)
+
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    if (lin >= a.tiles_m * a.tiles_n) return;
+    int mt, nt;
+    fused_tile(lin, a.tiles_m, a.tiles_n, mt, nt);
+    const int tid = threadIdx.x;
+    const int wave = wave_id();
+    const int lane = tid & 63;
+    const int q = lane & 31, hl = lane >> 5;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int H = a.H;
+    const int64_t T = a.total_T;
+    const int64_t row0 = (int64_t)mt * fused_out_rows<K>() - (K - 1);
+    const int n0 = nt * kWNC;
+
+    // row -> (sequence, position, length) map, before any load of the reduction (as in the kernel above)
+    {
+        const int64_t tf = row0 < 0 ? 0 : row0;
+        int lo = 0, hi = a.N;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
+        }
+        const int64_t c0 = a.cu[lo], c1 = a.cu[lo + 1];
+        if (tid < kFBM) {
+            const int64_t t = row0 + tid;
+            int pos = -1, len = 0, seq = lo;
+            if (c0 <= tf && c1 >= row0 + kFBM) {
+                if (t >= tf) { pos = (int)(t - c0); len = (int)(c1 - c0); }
+            } else if (t >= 0 && t < T) {
+                int l2 = 0, h2 = a.N;
+                while (h2 - l2 > 1) {
+                    const int mid = (l2 + h2) >> 1;
+                    if ((int64_t)a.cu[mid] <= t) l2 = mid; else h2 = mid;
+                }
+                seq = l2;
+                const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
+                if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
+            }
+            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq;
+        }
+    }
+
+    // ---------------------------------------------------------------- reduction
+    const int64_t vlo = row0 < 0 ? 0 : row0;
+    const int64_t vhi = (row0 + kFBM < T) ? row0 + kFBM : T;
+    // The row map above is filled under a branch that splits the waves; the
+    // descriptor size is taken through readfirstlane so that the compiler keeps
+    // it in SGPRs (otherwise every load gets a loop over distinct descriptors).
+    const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((vhi - vlo) * a.x_stride * 2));
+    const rsrc_t xr = row_rsrc(a.x + vlo * a.x_stride, xbytes);
+    const rsrc_t wr = row_rsrc(a.W, (uint32_t)((int64_t)3 * H * a.D * 2));
+    const int brow = lane >> 2;
+    const uint32_t bchunk = (uint32_t)(((lane & 3) ^ ((brow >> 2) & 3)) << 4);
+    uint32_t xoff[kWDmaA], woff[kWDmaB];
+#pragma unroll
+    for (int i = 0; i < kWDmaA; ++i) {
+        int64_t t = row0 + (wave + 8 * i) * 16 + brow;
+        t = t < vlo ? vlo : (t >= vhi ? vhi - 1 : t);
+        xoff[i] = (uint32_t)((t - vlo) * a.x_stride * 2) + bchunk;
+    }
+#pragma unroll
+    for (int i = 0; i < kWDmaB; ++i) {
+        const int n = (wave + 8 * i) * 16 + brow;      // staged W_in row: part n / 128, channel n % 128
+        const int chn = n0 + n % kWNC;                 // H % 128 == 0: every channel of the tile exists
+        woff[i] = (uint32_t)(((int64_t)(n / kWNC) * H + chn) * a.D * 2) + bchunk;
+    }
+    auto aslot = [&](auto u_c) -> uint8_t* {
+        constexpr int u = decltype(u_c)::value;
+        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else return ra2;
+    };
+    auto bslot = [&](auto u_c) -> uint8_t* {
+        constexpr int u = decltype(u_c)::value;
+        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else return rb2;
+    };
+    auto issue = [&](auto u_c, int kt) {
+        uint8_t* sa = aslot(u_c);
+        uint8_t* sb = bslot(u_c);
+        const uint32_t ko = (uint32_t)kt * kFRowBytes;
+#pragma unroll
+        for (int i = 0; i < kWDmaA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(sa + (wave + 8 * i) * 1024), 16, xoff[i] + ko,
+                                                     0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < kWDmaB; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(sb + (wave + 8 * i) * 1024), 16, woff[i] + ko,
+                                                     0, 0, 0);
+    };
+
+    f32x16 acc[4][3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    issue(IC<0>{}, 0);
+    issue(IC<1>{}, 1);
+    auto stage = [&](auto kt_c) {
+        constexpr int kt = decltype(kt_c)::value;
+        constexpr int u = kt % kWStages;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(kt + 1 < NK ? 1 : 0) * kWVm>();       // the next stage may still be in flight
+        stage_barrier();
+        if constexpr (kt + 2 < NK) issue(IC<(kt + 2) % kWStages>{}, kt + 2);
+        const uint8_t* sa = aslot(IC<u>{});
+        const uint8_t* sb = bslot(IC<u>{});
+#pragma unroll
+        for (int kk = 0; kk < kFBK / 16; ++kk) {
+            const int c = kk * 2 + hl;
+            bf16x8 fa[4], fb[3];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = *reinterpret_cast<const bf16x8*>(sa + lds_chunk(wm * 128 + i * 32 + q, c));
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_chunk(j * kWNC + wn * 32 + q, c));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        }
+        if constexpr (kt + 2 < NK) {                   // refill loads spread between the MFMAs
+#pragma unroll
+            for (int g = 0; g < kWVm; ++g) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_stages<0, NK>(stage);
+
+    // ---------------------------------------------------------------- epilogue
+    // As in the kernel above, one 32-row tile i at a time (the accumulators stay
+    // in AGPRs; this keeps the working set within the wave's 64 VGPRs).  Each
+    // wave stages its 128 x 32 outputs in its own 8 KiB of the (now idle) ring.
+    __syncthreads();
+    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : rb0));
+    uint16_t* wout = reinterpret_cast<uint16_t*>(region + (wave & 1) * kWRegion);   // [128][32]
+    const int lcn = wn * 32 + q;
+    const int ch = n0 + lcn;
+    const int rbase = wm * 128;
+    auto stage_out = [&](int i, int r, float v) {
+        wout[(i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3)) * 32 + q] = bf16_bits(v);
+    };
+    auto flush = [&](uint16_t* dst, int64_t stride) {
+        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));   // this wave's LDS writes
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < 128 * 4 / 64; ++k) {
+            const int id = lane + 64 * k;
+            const int rw = id >> 2, cc = id & 3;
+            const int row = rbase + rw;
+            if (row >= K - 1 && s_pos[row] >= 0) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(wout + rw * 32 + cc * 8);
+                *reinterpret_cast<u32x4*>(dst + (row0 + row) * stride + n0 + wn * 32 + cc * 8) = v;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));
+        __builtin_amdgcn_wave_barrier();
+    };
+    if (a.io != nullptr) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) stage_out(i, r, acc[i][j][r]);
+            flush(a.io + (int64_t)j * H, a.io_stride);
+        }
+    }
+    // history entering the second row half: bx of rows 125..127 from the first half's waves
+    if (wm == 0 && hl == 1) {
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) {
+            const int r = 12 + 4 - (K - 1) + m;
+            s_edge[wn][q][m] = acc[3][0][r] * acc[3][2][r];
+        }
+    }
+    lds_barrier();
+
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
+    const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
+    auto s0 = [&](int seq, int idx) -> float {
+        if (a.pool == nullptr) return 0.f;
+        const int64_t slot_id = a.slot_idx[seq];
+        if (!slot_ok(slot_id, a.num_slots)) return 0.f;
+        return bf16_val(a.pool[slot_id * a.slot_stride + (int64_t)ch * K + idx]);
+    };
+    const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
+    const bool simple = p0 >= 0 && pl == p0 + kFBM - 1 && !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
+    float prev[K > 1 ? K - 1 : 1];                     // the partner's last K-1 rows of the previous quad
+#pragma unroll
+    for (int m = 0; m < K - 1; ++m) prev[m] = wm == 1 ? s_edge[wn][q][m] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float bx[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bx[r] = acc[i][0][r] * acc[i][2][r];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float tl[K > 1 ? K - 1 : 1];
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) tl[m] = __shfl_xor(bx[4 * g + 4 - (K - 1) + m], 32);
+            float hx[K - 1 + 4];
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) hx[m] = hl ? tl[m] : prev[m];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) hx[K - 1 + j] = bx[4 * g + j];
+#pragma unroll
+            for (int m = 0; m < K - 1; ++m) prev[m] = tl[m];
+            const int R0 = rbase + i * 32 + 8 * g + 4 * hl;
+            if (simple) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
+#pragma unroll
+                    for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], hx[j + k], conv);
+                    stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
+                }
+            } else {
+                const int4 p = *reinterpret_cast<const int4*>(s_pos + R0);
+                const int pos4[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = R0 + j;
+                    const int pos = pos4[j];
+                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
+#pragma unroll
+                    for (int k = 0; k < K - 1; ++k) {
+                        const int d = K - 1 - k;
+                        float h = hx[j + k];
+                        if (pos < d) h = (pos >= 0 && row >= K - 1) ? s0(s_seq[row], pos + 1 + k) : 0.f;
+                        conv = fmaf(wk[k], h, conv);
+                    }
+                    stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
+                    if (a.fin != nullptr && row >= K - 1 && pos >= 0 && pos == s_len[row] - 1) {
+                        const int len = pos + 1, seq = s_seq[row];
+                        uint16_t* f = a.fin + (int64_t)seq * H * K + (int64_t)ch * K;
+#pragma unroll
+                        for (int e = 0; e < K; ++e) {
+                            const int idx = len + e;
+                            f[e] = bf16_bits(idx >= K ? hx[j + e] : s0(seq, idx));
+                        }
+                    }
+                }
+            }
+        }
+    }
+    flush(a.y, a.y_stride);
+}
+
 // Installs the staged final states: slot_idx[i] <- fin[i] for every sequence
 // with at least one token (an empty sequence leaves its slot as it was).
 __global__ __launch_bounds__(kSmallBlock) void fused_state_commit_kernel(const FusedArgs a, int K) {
@@ -479,17 +772,31 @@ static void fused_launch_main(const FusedArgs& a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((fused_prefill_kernel<K, NK>), dim3(blocks), dim3(kFThreads), 0, s, a);
 }
 
+template <int K, int NK>
+static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((fused_wide_kernel<K, NK>), dim3(blocks), dim3(kWThreads), 0, s, a);
+}
+
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
     const int64_t out = fused_out_rows<K>();
     a.tiles_m = (int)((a.total_T + out - 1) / out);
-    a.tiles_n = a.H / kFNC;
+    const bool wide = a.H % kWNC == 0 && (a.D == 1024 || a.D == 1536 || a.D == 2048);
+    a.tiles_n = a.H / (wide ? kWNC : kFNC);
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
-    switch (a.D) {      // straight-line reductions for the LFM2 hidden sizes
-        case 1024: fused_launch_main<K, 1024 / kFBK>(a, blocks, s); break;
-        case 1536: fused_launch_main<K, 1536 / kFBK>(a, blocks, s); break;
-        case 2048: fused_launch_main<K, 2048 / kFBK>(a, blocks, s); break;
-        default: fused_launch_main<K, 0>(a, blocks, s); break;
+    if (wide) {
+        switch (a.D) {
+            case 1024: fused_launch_wide<K, 1024 / kFBK>(a, blocks, s); break;
+            case 1536: fused_launch_wide<K, 1536 / kFBK>(a, blocks, s); break;
+            default: fused_launch_wide<K, 2048 / kFBK>(a, blocks, s); break;
+        }
+    } else {
+        switch (a.D) {      // straight-line reductions for the LFM2 hidden sizes
+            case 1024: fused_launch_main<K, 1024 / kFBK>(a, blocks, s); break;
+            case 1536: fused_launch_main<K, 1536 / kFBK>(a, blocks, s); break;
+            case 2048: fused_launch_main<K, 2048 / kFBK>(a, blocks, s); break;
+            default: fused_launch_main<K, 0>(a, blocks, s); break;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.fin == nullptr) return e;

@@ -146,3 +146,25 @@ def test_fused_deterministic():
     b = _run(c, with_io=True)
     for u, v, n in zip(a, b, ("y", "in_proj", "pool")):
         assert_bits(u, v, f"rerun {n}")
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("H", [128, 256])
+def test_fused_wide_tiles(K, H):
+    """Channel counts that are multiples of 128 with D = 1024 run the 8-wave wide tile (256 rows x 128 channels):
+    ragged sequences, ones shorter than K, a sequence across several row tiles, rows after the last sequence,
+    padded x / y / in_proj rows, a pool and a bias."""
+    lens = [37, 1, 0, 300, 5, 2, 1, 2, 3, 600]
+    _say(f"case: fused wide tile K={K} H={H} D=1024 lens={lens} padded, tail rows")
+    c = wl.fused_case(520 + K + H, lens, H=H, K=K, D=1024, slots=len(lens) + 2, bias=True, x_pad=8, tail_rows=5)
+    y, io, pool = _run(c, with_io=True, y_pad=8, io_pad=16)
+    _check(c, y, io, pool, f"wide K={K} H={H}")
+
+
+@pytest.mark.parametrize("D", [1536, 2048])
+def test_fused_wide_other_depths(D):
+    """The wide tile's straight-line reductions for the other LFM2 hidden sizes, no pool."""
+    _say(f"case: fused wide tile D={D} H=128 one sequence")
+    c = wl.fused_case(530 + D, [777], H=128, K=3, D=D)
+    y, io, pool = _run(c, with_io=True)
+    _check(c, y, io, pool, f"wide D={D}")
