@@ -85,32 +85,88 @@ def read_traffic(per_launch_algo_bytes):
         return None
 
 
-def cpu_baseline(wl_mod, T, H, K, n_channels, min_seconds=10.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl_mod, T, H, K, n_channels, min_seconds=10.0, single_channels=64):
     """The fp64 oracle (as it stands) on the same workload restricted to n_channels channels
-    (channels are independent, so this is the same arithmetic on a slice)."""
+    (channels are independent, so this is the same arithmetic on a slice).  Whole passes with
+    min(16, available) OpenMP threads until min_seconds have elapsed (value: median pass), then
+    three single-threaded passes over the first `single_channels` channels (median)."""
+    import statistics
     import torch
     import oracle
     c = wl_mod.train_lfm2(T=T)
-    chans = torch.arange(n_channels)
-    cols = torch.cat([chans, chans + H, chans + 2 * H])
-    inp = oracle.f64(c.inp[:, cols])
-    w = oracle.f64(c.w[chans])
-    dy = oracle.f64(c.dy[:, chans])
-    threads = min(16, len(os.sched_getaffinity(0)))
-    oracle.set_threads(threads)
-    # whole passes until at least min_seconds of CPU work have been timed
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def sample(n):
+        chans = torch.arange(n)
+        cols = torch.cat([chans, chans + H, chans + 2 * H])
+        return oracle.f64(c.inp[:, cols]), oracle.f64(c.w[chans]), oracle.f64(c.dy[:, chans])
+
+    def one_pass(inp, w, dy):
+        t = time.perf_counter()
         oracle.prefill(inp, c.cu, w)
         oracle.backward(inp, c.cu, w, dy)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds:
+        return time.perf_counter() - t
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    oracle.set_threads(threads)
+    inp, w, dy = sample(n_channels)
+    times, t0 = [], time.perf_counter()
+    while True:
+        times.append(one_pass(inp, w, dy))
+        if time.perf_counter() - t0 >= min_seconds:
             break
-    nbytes = (algo_bytes_fwd(T, n_channels, K, 2) + algo_bytes_bwd(T, n_channels, K, 2)) * reps
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+    dt = time.perf_counter() - t0
+    pass_bytes = algo_bytes_fwd(T, n_channels, K, 2) + algo_bytes_bwd(T, n_channels, K, 2)
+    med = statistics.median(times)
+    oracle.set_threads(1)
+    inp1, w1, dy1 = sample(single_channels)
+    t1 = statistics.median([one_pass(inp1, w1, dy1) for _ in range(3)])
+    oracle.set_threads(threads)
+    bytes1 = algo_bytes_fwd(T, single_channels, K, 2) + algo_bytes_bwd(T, single_channels, K, 2)
+    return {"value": round(pass_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"fwd+bwd, T={T}, first {n_channels} of {H} channels, K={K}, bf16 inputs widened to fp64; "
-                      f"{reps} passes in {dt:.2f} s wall", "seconds": round(dt, 3), "passes": reps}
+                      f"median of {len(times)} passes ({dt:.2f} s wall)",
+            "seconds": round(dt, 3), "passes": len(times), "pass_s_median": round(med, 4),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(bytes1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"first {single_channels} channels, median of 3 passes",
+                              "pass_s_median": round(t1, 4)}}
+
+
+def copy_ceiling(reps=10):
+    """Measured device-copy ceiling: a plain 1 GiB device-to-device copy (torch's copy kernel), bytes read +
+    written per copy over its event time, median of `reps`."""
+    import statistics
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    ms = statistics.median(ts)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": round(2 * n / ms / 1e6, 1), "bytes_per_copy": 2 * n, "ms": round(ms, 5),
+            "kernel": "torch copy_ of 1 GiB, device to device", "reps": reps}
 
 
 def timed_loop(fn, steps, warmup):
@@ -369,6 +425,19 @@ def main():
     ms_step = start.elapsed_time(stop) / args.steps
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
     bwd_ms = sum(b.elapsed_time(cc) for _, b, cc in ev) / args.steps
+    # the median protocol beside the timed loop: 50 more steps, each call bracketed by events
+    import statistics
+    ev50 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
+    for s in range(50):
+        ev50[s][0].record()
+        fwd()
+        ev50[s][1].record()
+        bwd()
+        ev50[s][2].record()
+    torch.cuda.synchronize()
+    median50 = {"fwd_ms": round(statistics.median(a.elapsed_time(b) for a, b, _ in ev50), 5),
+                "bwd_ms": round(statistics.median(b.elapsed_time(cc) for _, b, cc in ev50), 5),
+                "step_ms": round(statistics.median(a.elapsed_time(cc) for a, _, cc in ev50), 5), "reps": 50}
     step_bytes = algo_bytes_fwd(T, H, K, e) + algo_bytes_bwd(T, H, K, e)
     bwd_bytes = algo_bytes_bwd(T, H, K, e)
     value = step_bytes / ms_step / 1e6
@@ -399,8 +468,13 @@ def main():
                      "frac": round(bwd_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "lfm2sc_backward (backward_kernel + dw_finish_kernel, one call)",
                      "algorithmic_bytes_per_launch": bwd_bytes},
+        "median_of_50": median50,
         "context": {"pages_mi325x_liger_fwd_bwd_ms": {"T=4096": 0.463, "T=65536": 8.083}},
     }
+    cc = copy_ceiling()
+    cc["step_frac"] = round(value / cc["GB/s"], 4)
+    cc["backward_frac"] = round(bwd_gbs / cc["GB/s"], 4)
+    line["copy_ceiling"] = cc
     if args.extra:
         line["extra"] = extra_measurements(wl, max(2, args.steps // 2))
     if not args.no_cpu:

@@ -129,6 +129,70 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int v> using IC = std::integral_constant<int, v>;
 
+// Per-row sequence data of a tile's epilogue (LDS): position in the sequence
+// (-1 outside every sequence), sequence length and index, and the row's slot
+// when a pool is given and the slot id is in range (else -1).
+struct RowMap {
+    const int* pos;
+    const int* len;
+    const int* seq;
+    const int* slot;
+};
+
+// The general (multi-sequence) epilogue for the 4 consecutive rows R0..R0+3
+// that one lane holds in an accumulator quad.  hx holds bx of rows R0-(K-1) ..
+// R0+3; cgate the rows' C.  Rows whose conv history reaches before their
+// sequence start take initial-state entries instead (X[pos+1+k], k < K-1);
+// those entries are fetched first, all together, from an address chosen
+// without branching (an entry that is not needed reads the channel's weight
+// instead), so the loads overlap rather than queue one behind another.  Each
+// row's effective history then serves both its conv and, at a sequence end,
+// its final state X[len .. len+K-1].
+template <int K, typename Out>
+__device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& rm, int R0, int ch,
+                                             const float (&wk)[K], float bv, const float* hx, const float* cgate,
+                                             Out&& out) {
+    constexpr int KH = K > 1 ? K - 1 : 1;
+    const int4 p4 = *reinterpret_cast<const int4*>(rm.pos + R0);
+    const int pos[4] = {p4.x, p4.y, p4.z, p4.w};
+    float sv[4][KH];
+    if (a.pool != nullptr) {
+        const int4 s4 = *reinterpret_cast<const int4*>(rm.slot + R0);
+        const int slot[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) {
+                const bool need = pos[j] >= 0 && pos[j] < K - 1 - k && R0 + j >= K - 1 && slot[j] >= 0;
+                const uint16_t* src = need ? a.pool + (int64_t)slot[j] * a.slot_stride + (int64_t)ch * K + pos[j] + 1 + k
+                                           : a.w + (int64_t)ch * K;
+                sv[j][k] = need ? bf16_val(*src) : 0.f;
+            }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int k = 0; k < KH; ++k) sv[j][k] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float h[KH];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) h[k] = pos[j] < K - 1 - k ? sv[j][k] : hx[j + k];
+        float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], h[k], conv);
+        out(j, cgate[j] * conv);
+        const int row = R0 + j;
+        if (a.fin != nullptr && row >= K - 1 && pos[j] >= 0 && pos[j] == rm.len[row] - 1) {
+            uint16_t* f = a.fin + (int64_t)rm.seq[row] * a.H * K + (int64_t)ch * K;
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) f[e] = bf16_bits(h[e]);
+            f[K - 1] = bf16_bits(hx[K - 1 + j]);
+        }
+    }
+}
+
 // NK: number of kFBK stages along D when it is known at compile time (the
 // reduction is then straight-line code), 0 for the loop form.
 template <int K, int NK>
@@ -140,6 +204,7 @@ void fused_prefill_kernel(const FusedArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ost[kFBM * kFOutStride];
     __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
     __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
     __shared__ float s_edge[2][32][4];        // bx of rows 125..127 of each channel (the second half's history)
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
@@ -170,6 +235,7 @@ void fused_prefill_kernel(const FusedArgs a) {
             if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
         }
         const int64_t c0 = a.cu[lo], c1 = a.cu[lo + 1];
+        const int slot_lo = a.pool != nullptr ? a.slot_idx[lo] : -1;   // loaded beside c0, c1
         const int64_t t = row0 + tid;
         int pos = -1, len = 0, seq = lo;
         if (c0 <= tf && c1 >= row0 + kFBM) {       // one sequence holds rows [tf, row0 + 256)
@@ -184,7 +250,12 @@ void fused_prefill_kernel(const FusedArgs a) {
             const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
             if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
         }
-        s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq;
+        int sid = -1;                              // the row's slot, if it has one in range
+        if (a.pool != nullptr && pos >= 0) {
+            const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
+            sid = slot_ok(v, a.num_slots) ? (int)v : -1;
+        }
+        s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
     }
 
     // ---------------------------------------------------------------- reduction
@@ -376,13 +447,7 @@ void fused_prefill_kernel(const FusedArgs a) {
 #pragma unroll
     for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
     const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
-    // Entry idx (1 <= idx < K) of sequence seq's initial state for this channel.
-    auto s0 = [&](int seq, int idx) -> float {
-        if (a.pool == nullptr) return 0.f;
-        const int64_t slot_id = a.slot_idx[seq];
-        if (!slot_ok(slot_id, a.num_slots)) return 0.f;
-        return bf16_val(a.pool[slot_id * a.slot_stride + (int64_t)ch * K + idx]);
-    };
+    const RowMap rm{s_pos, s_len, s_seq, s_slot};
     // hx[m] = bx of row R0 - (K-1) + m for quad (i, g): K-1 history rows, then the quad's own 4
     auto history = [&](int i, int g, float* hx) {
 #pragma unroll
@@ -423,33 +488,10 @@ void fused_prefill_kernel(const FusedArgs a) {
                 const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
                 float hx[K - 1 + 4];
                 history(i, g, hx);
-                const int4 p = *reinterpret_cast<const int4*>(s_pos + R0);
-                const int pos4[4] = {p.x, p.y, p.z, p.w};
+                float cg[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = R0 + j;
-                    const int pos = pos4[j];
-                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
-#pragma unroll
-                    for (int k = 0; k < K - 1; ++k) {
-                        const int d = K - 1 - k;         // X[pos+1+k] is bx of the token d rows back
-                        float h = hx[j + k];
-                        if (pos < d) h = (pos >= 0 && row >= K - 1) ? s0(s_seq[row], pos + 1 + k) : 0.f;
-                        conv = fmaf(wk[k], h, conv);
-                    }
-                    stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
-                    if (a.fin != nullptr && row >= K - 1 && pos >= 0 && pos == s_len[row] - 1) {
-                        // final state X[len .. len+K-1]: bx of the last tokens (rows row-K+1+e,
-                        // i.e. hx[j + e]), or initial-state entries
-                        const int len = pos + 1, seq = s_seq[row];
-                        uint16_t* f = a.fin + (int64_t)seq * H * K + (int64_t)ch * K;
-#pragma unroll
-                        for (int e = 0; e < K; ++e) {
-                            const int idx = len + e;
-                            f[e] = bf16_bits(idx >= K ? hx[j + e] : s0(seq, idx));
-                        }
-                    }
-                }
+                for (int j = 0; j < 4; ++j) cg[j] = acc[i][1][4 * g + j];
+                quad_general<K>(a, rm, R0, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
             }
     }
     flush_rows(a.y, a.y_stride, true);
@@ -488,6 +530,7 @@ void fused_wide_kernel(const FusedArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB];
     __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
     __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
     __shared__ float s_edge[4][32][4];           // bx of rows 125..127 per channel group (the second half's history)
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
@@ -513,6 +556,7 @@ void fused_wide_kernel(const FusedArgs a) {
             if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
         }
         const int64_t c0 = a.cu[lo], c1 = a.cu[lo + 1];
+        const int slot_lo = a.pool != nullptr ? a.slot_idx[lo] : -1;   // loaded beside c0, c1
         if (tid < kFBM) {
             const int64_t t = row0 + tid;
             int pos = -1, len = 0, seq = lo;
@@ -528,7 +572,12 @@ void fused_wide_kernel(const FusedArgs a) {
                 const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
                 if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
             }
-            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq;
+            int sid = -1;                              // the row's slot, if it has one in range
+            if (a.pool != nullptr && pos >= 0) {
+                const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
+                sid = slot_ok(v, a.num_slots) ? (int)v : -1;
+            }
+            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
         }
     }
 
@@ -677,12 +726,7 @@ void fused_wide_kernel(const FusedArgs a) {
 #pragma unroll
     for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
     const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
-    auto s0 = [&](int seq, int idx) -> float {
-        if (a.pool == nullptr) return 0.f;
-        const int64_t slot_id = a.slot_idx[seq];
-        if (!slot_ok(slot_id, a.num_slots)) return 0.f;
-        return bf16_val(a.pool[slot_id * a.slot_stride + (int64_t)ch * K + idx]);
-    };
+    const RowMap rm{s_pos, s_len, s_seq, s_slot};
     const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
     const bool simple = p0 >= 0 && pl == p0 + kFBM - 1 && !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
     float prev[K > 1 ? K - 1 : 1];                     // the partner's last K-1 rows of the previous quad
@@ -715,31 +759,10 @@ void fused_wide_kernel(const FusedArgs a) {
                     stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
                 }
             } else {
-                const int4 p = *reinterpret_cast<const int4*>(s_pos + R0);
-                const int pos4[4] = {p.x, p.y, p.z, p.w};
+                float cg[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int row = R0 + j;
-                    const int pos = pos4[j];
-                    float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
-#pragma unroll
-                    for (int k = 0; k < K - 1; ++k) {
-                        const int d = K - 1 - k;
-                        float h = hx[j + k];
-                        if (pos < d) h = (pos >= 0 && row >= K - 1) ? s0(s_seq[row], pos + 1 + k) : 0.f;
-                        conv = fmaf(wk[k], h, conv);
-                    }
-                    stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
-                    if (a.fin != nullptr && row >= K - 1 && pos >= 0 && pos == s_len[row] - 1) {
-                        const int len = pos + 1, seq = s_seq[row];
-                        uint16_t* f = a.fin + (int64_t)seq * H * K + (int64_t)ch * K;
-#pragma unroll
-                        for (int e = 0; e < K; ++e) {
-                            const int idx = len + e;
-                            f[e] = bf16_bits(idx >= K ? hx[j + e] : s0(seq, idx));
-                        }
-                    }
-                }
+                for (int j = 0; j < 4; ++j) cg[j] = acc[i][1][4 * g + j];
+                quad_general<K>(a, rm, R0, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
             }
         }
     }
