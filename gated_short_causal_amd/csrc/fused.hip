@@ -506,7 +506,7 @@ void fused_prefill_kernel(const FusedArgs a) {
 // H % 128 == 0 and D is one of the unrolled hidden sizes.
 constexpr int kWNC = 128;                          // channels per wide tile
 constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
-constexpr int kWStages = 3;                        // ring depth: 2 stages in flight ahead of the one in use
+constexpr int kWStages = 4;                        // ring depth: 3 stages in flight ahead of the one in use
 constexpr int kWStageA = kFBM * kFRowBytes;        // 16 KiB of x rows
 constexpr int kWStageB = 3 * kWNC * kFRowBytes;    // 24 KiB of W_in rows
 constexpr int kWDmaA = kFBM / 16 / 8;              // 2 blocks of 16 x rows per wave
@@ -526,12 +526,11 @@ template <int K, int NK>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fused_wide_kernel(const FusedArgs a) {
     static_assert(NK >= 2, "at least two stages");
-    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA];
-    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB];
-    __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
-    __shared__ int s_len[kFBM], s_seq[kFBM];
-    __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
-    __shared__ float s_edge[4][32][4];           // bx of rows 125..127 per channel group (the second half's history)
+    // The ring takes all 160 KiB of LDS.  The row map is held in registers
+    // (threads 0..255, one row each) during the reduction and moves into the
+    // idle ring afterwards, with the hand-off of the row-half boundary.
+    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA], ra3[kWStageA];
+    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB], rb3[kWStageB];
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
     if (lin >= a.tiles_m * a.tiles_n) return;
@@ -547,7 +546,9 @@ void fused_wide_kernel(const FusedArgs a) {
     const int64_t row0 = (int64_t)mt * fused_out_rows<K>() - (K - 1);
     const int n0 = nt * kWNC;
 
-    // row -> (sequence, position, length) map, before any load of the reduction (as in the kernel above)
+    // row -> (sequence, position, length, slot) map, before any load of the
+    // reduction (as in the kernel above); kept in registers until the epilogue
+    int m_pos = -1, m_len = 0, m_seq = 0, m_slot = -1;
     {
         const int64_t tf = row0 < 0 ? 0 : row0;
         int lo = 0, hi = a.N;
@@ -577,7 +578,7 @@ void fused_wide_kernel(const FusedArgs a) {
                 const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
                 sid = slot_ok(v, a.num_slots) ? (int)v : -1;
             }
-            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
+            m_pos = pos; m_len = len; m_seq = seq; m_slot = sid;
         }
     }
 
@@ -607,11 +608,13 @@ void fused_wide_kernel(const FusedArgs a) {
     }
     auto aslot = [&](auto u_c) -> uint8_t* {
         constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else return ra2;
+        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else if constexpr (u == 2) return ra2;
+        else return ra3;
     };
     auto bslot = [&](auto u_c) -> uint8_t* {
         constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else return rb2;
+        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else if constexpr (u == 2) return rb2;
+        else return rb3;
     };
     auto issue = [&](auto u_c, int kt) {
         uint8_t* sa = aslot(u_c);
@@ -637,13 +640,15 @@ void fused_wide_kernel(const FusedArgs a) {
 
     issue(IC<0>{}, 0);
     issue(IC<1>{}, 1);
+    if constexpr (NK > 2) issue(IC<2>{}, 2);
     auto stage = [&](auto kt_c) {
         constexpr int kt = decltype(kt_c)::value;
         constexpr int u = kt % kWStages;
+        constexpr int later = NK - 1 - kt < kWStages - 2 ? NK - 1 - kt : kWStages - 2;   // stages after kt in flight
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(kt + 1 < NK ? 1 : 0) * kWVm>();       // the next stage may still be in flight
+        wait_vm<later * kWVm>();
         stage_barrier();
-        if constexpr (kt + 2 < NK) issue(IC<(kt + 2) % kWStages>{}, kt + 2);
+        if constexpr (kt + kWStages - 1 < NK) issue(IC<(kt + kWStages - 1) % kWStages>{}, kt + kWStages - 1);
         const uint8_t* sa = aslot(IC<u>{});
         const uint8_t* sb = bslot(IC<u>{});
 #pragma unroll
@@ -662,7 +667,7 @@ void fused_wide_kernel(const FusedArgs a) {
                 for (int j = 0; j < 3; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if constexpr (kt + 2 < NK) {                   // refill loads spread between the MFMAs
+        if constexpr (kt + kWStages - 1 < NK) {        // refill loads spread between the MFMAs
 #pragma unroll
             for (int g = 0; g < kWVm; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -674,11 +679,29 @@ void fused_wide_kernel(const FusedArgs a) {
     unroll_stages<0, NK>(stage);
 
     // ---------------------------------------------------------------- epilogue
-    // As in the kernel above, one 32-row tile i at a time (the accumulators stay
-    // in AGPRs; this keeps the working set within the wave's 64 VGPRs).  Each
-    // wave stages its 128 x 32 outputs in its own 8 KiB of the (now idle) ring.
+    // As in the kernel above, one 32-row tile i at a time, which keeps the
+    // working set beside the 192 accumulator registers small.  Each wave stages
+    // its 128 x 32 outputs in its own 8 KiB of the x slots of the (now idle)
+    // ring; the row map goes to the last W_in slot, the row-half hand-off (bx
+    // of rows 125..127 of the first half, per channel) to the one before.
     __syncthreads();
-    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : rb0));
+    int* s_pos = reinterpret_cast<int*>(rb3);
+    int* s_len = s_pos + kFBM;
+    int* s_seq = s_len + kFBM;
+    int* s_slot = s_seq + kFBM;
+    float (*s_edge)[32][4] = reinterpret_cast<float (*)[32][4]>(rb2);
+    if (tid < kFBM) {
+        s_pos[tid] = m_pos; s_len[tid] = m_len; s_seq[tid] = m_seq; s_slot[tid] = m_slot;
+    }
+    if (wm == 0 && hl == 1) {
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) {
+            const int r = 12 + 4 - (K - 1) + m;
+            s_edge[wn][q][m] = acc[3][0][r] * acc[3][2][r];
+        }
+    }
+    lds_barrier();
+    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : ra3));
     uint16_t* wout = reinterpret_cast<uint16_t*>(region + (wave & 1) * kWRegion);   // [128][32]
     const int lcn = wn * 32 + q;
     const int ch = n0 + lcn;
@@ -712,15 +735,6 @@ void fused_wide_kernel(const FusedArgs a) {
             flush(a.io + (int64_t)j * H, a.io_stride);
         }
     }
-    // history entering the second row half: bx of rows 125..127 from the first half's waves
-    if (wm == 0 && hl == 1) {
-#pragma unroll
-        for (int m = 0; m < K - 1; ++m) {
-            const int r = 12 + 4 - (K - 1) + m;
-            s_edge[wn][q][m] = acc[3][0][r] * acc[3][2][r];
-        }
-    }
-    lds_barrier();
 
     float wk[K];
 #pragma unroll
