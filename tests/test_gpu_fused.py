@@ -168,3 +168,48 @@ def test_fused_wide_other_depths(D):
     c = wl.fused_case(530 + D, [777], H=128, K=3, D=D)
     y, io, pool = _run(c, with_io=True)
     _check(c, y, io, pool, f"wide D={D}")
+
+
+def test_fused_graph_replays_match_eager():
+    """The fused call with a pool (tile kernel + state install kernel) and the in_proj output, captured in a
+    HIP graph: each replay, with eager work and syncs in between and the pool restored first, must reproduce
+    the eager results bit for bit."""
+    lens = [300, 1, 0, 77, 2]
+    _say(f"case: fused graph capture lens={lens} H=256 D=1024")
+    c = wl.fused_case(540, lens, H=256, K=3, D=1024, slots=7, bias=True)
+    g = c.to(DEV)
+    T, N = c.x.shape[0], len(lens)
+    pool0 = g.pool.clone()
+    y = torch.empty(T, c.H, dtype=BF, device=DEV)
+    io = torch.empty(T, 3 * c.H, dtype=BF, device=DEV)
+    ws = torch.empty(lfm2sc_fused_prefill_workspace_bytes(BF, c.H, c.K, N, True), dtype=torch.uint8, device=DEV)
+
+    def call():
+        lfm2sc_fused_prefill(g.x, g.W_in, g.cu, g.w, y, g.pool, g.slot_idx, bias=g.bias, in_proj_out=io,
+                             workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (y, io, g.pool)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.pool.copy_(pool0)
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    g.pool.copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        io.fill_(float("nan"))
+        g.pool.copy_(pool0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "in_proj_out", "pool"), (y, io, g.pool), ref):
+            assert_bits(a, b, f"replay {rep}: {name}")
+    _check(c, ref[0].cpu(), ref[1].cpu(), ref[2].cpu(), "graph")
