@@ -41,6 +41,7 @@
 // them to a per-sequence staging block, and a second small kernel installs
 // them into the slots after every tile has read its initial states (a slot may
 // be read by one tile and written by another).
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.hpp"
@@ -74,6 +75,16 @@ __device__ __forceinline__ uint16_t bf16_bits(float f) {
     return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2)) & 0xffffu);
 }
 __device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// c + sum of the 8 products a[e] * b[e] (bf16 operands, fp32 accumulation)
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const bf16x8& b, float c) {
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), c, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), c,
+                                           false);
+}
 
 // Swizzled byte offset of 16-byte chunk c of staged row r: rows r, r+4, r+8,
 // r+12 put chunk c in four different positions, so the 16 lanes of a
@@ -140,7 +151,8 @@ struct RowMap {
 };
 
 // The general (multi-sequence) epilogue for the 4 consecutive rows R0..R0+3
-// that one lane holds in an accumulator quad.  hx holds bx of rows R0-(K-1) ..
+// that one lane holds in an accumulator quad (rows before first_out are the
+// tile's history rows, not outputs).  hx holds bx of rows R0-(K-1) ..
 // R0+3; cgate the rows' C.  Rows whose conv history reaches before their
 // sequence start take initial-state entries instead (X[pos+1+k], k < K-1);
 // those entries are fetched first, all together, from an address chosen
@@ -149,7 +161,7 @@ struct RowMap {
 // row's effective history then serves both its conv and, at a sequence end,
 // its final state X[len .. len+K-1].
 template <int K, typename Out>
-__device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& rm, int R0, int ch,
+__device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& rm, int R0, int first_out, int ch,
                                              const float (&wk)[K], float bv, const float* hx, const float* cgate,
                                              Out&& out) {
     constexpr int KH = K > 1 ? K - 1 : 1;
@@ -163,7 +175,7 @@ __device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& r
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int k = 0; k < K - 1; ++k) {
-                const bool need = pos[j] >= 0 && pos[j] < K - 1 - k && R0 + j >= K - 1 && slot[j] >= 0;
+                const bool need = pos[j] >= 0 && pos[j] < K - 1 - k && R0 + j >= first_out && slot[j] >= 0;
                 const uint16_t* src = need ? a.pool + (int64_t)slot[j] * a.slot_stride + (int64_t)ch * K + pos[j] + 1 + k
                                            : a.w + (int64_t)ch * K;
                 sv[j][k] = need ? bf16_val(*src) : 0.f;
@@ -184,7 +196,7 @@ __device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& r
         for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], h[k], conv);
         out(j, cgate[j] * conv);
         const int row = R0 + j;
-        if (a.fin != nullptr && row >= K - 1 && pos[j] >= 0 && pos[j] == rm.len[row] - 1) {
+        if (a.fin != nullptr && row >= first_out && pos[j] >= 0 && pos[j] == rm.len[row] - 1) {
             uint16_t* f = a.fin + (int64_t)rm.seq[row] * a.H * K + (int64_t)ch * K;
 #pragma unroll
             for (int e = 0; e < K - 1; ++e) f[e] = bf16_bits(h[e]);
@@ -491,7 +503,7 @@ void fused_prefill_kernel(const FusedArgs a) {
                 float cg[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cg[j] = acc[i][1][4 * g + j];
-                quad_general<K>(a, rm, R0, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
+                quad_general<K>(a, rm, R0, K - 1, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
             }
     }
     flush_rows(a.y, a.y_stride, true);
@@ -504,9 +516,19 @@ void fused_prefill_kernel(const FusedArgs a) {
 // waves (two per SIMD), each wave still 128 rows x 32 channels, so a stage
 // moves 40 KiB for twice the MFMA work (1.4x less data per FLOP).  Used when
 // H % 128 == 0 and D is one of the unrolled hidden sizes.
+//
+// Two forms (HALO).  Without, consecutive tiles overlap by K-1 rows as above.
+// With, a tile outputs all 256 of its rows, so T = 4096 fills exactly one
+// round of 256 CUs instead of spilling 16 tiles into a second; the conv
+// history of its first K-1 rows is bx of the K-1 x rows just before it ("halo
+// rows"): they are staged in LDS once per tile, and the waves of the first row
+// half form their B and xv with bf16 dot products against the W_in fragments
+// they already hold for the MFMAs, stage by stage (fp32 accumulation, no extra
+// W_in traffic).  That work makes a tile ~14% slower on MI355X, so the
+// launcher takes the halo form only when it saves enough rounds of tiles.
 constexpr int kWNC = 128;                          // channels per wide tile
 constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
-constexpr int kWStages = 4;                        // ring depth: 3 stages in flight ahead of the one in use
+constexpr int kWStages = 3;                        // ring depth: 2 stages in flight ahead of the one in use
 constexpr int kWStageA = kFBM * kFRowBytes;        // 16 KiB of x rows
 constexpr int kWStageB = 3 * kWNC * kFRowBytes;    // 24 KiB of W_in rows
 constexpr int kWDmaA = kFBM / 16 / 8;              // 2 blocks of 16 x rows per wave
@@ -522,15 +544,21 @@ __device__ __forceinline__ void unroll_stages(F& f) {
     }
 }
 
-template <int K, int NK>
+template <int K, int NK, bool HALO>
 __global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fused_wide_kernel(const FusedArgs a) {
     static_assert(NK >= 2, "at least two stages");
-    // The ring takes all 160 KiB of LDS.  The row map is held in registers
-    // (threads 0..255, one row each) during the reduction and moves into the
-    // idle ring afterwards, with the hand-off of the row-half boundary.
-    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA], ra3[kWStageA];
-    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB], rb3[kWStageB];
+    constexpr int KH = K > 1 ? K - 1 : 1;
+    constexpr int kRowBytes = NK * kFRowBytes;         // one x row: D bf16
+    constexpr bool kHalo = HALO && K > 1;
+    constexpr int kFirstOut = kHalo ? 0 : K - 1;       // rows before it are history, not outputs
+    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA];
+    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_halo[kHalo ? KH * kRowBytes : 16];   // x of the halo rows
+    __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
+    __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
+    __shared__ float s_edge[4][32][4];           // bx of rows 125..127 per channel group (the second half's history)
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
     if (lin >= a.tiles_m * a.tiles_n) return;
@@ -543,12 +571,11 @@ void fused_wide_kernel(const FusedArgs a) {
     const int wm = wave >> 2, wn = wave & 3;
     const int H = a.H;
     const int64_t T = a.total_T;
-    const int64_t row0 = (int64_t)mt * fused_out_rows<K>() - (K - 1);
+    const int64_t row0 = kHalo ? (int64_t)mt * kFBM : (int64_t)mt * fused_out_rows<K>() - (K - 1);
     const int n0 = nt * kWNC;
 
     // row -> (sequence, position, length, slot) map, before any load of the
-    // reduction (as in the kernel above); kept in registers until the epilogue
-    int m_pos = -1, m_len = 0, m_seq = 0, m_slot = -1;
+    // reduction (as in the kernel above)
     {
         const int64_t tf = row0 < 0 ? 0 : row0;
         int lo = 0, hi = a.N;
@@ -578,7 +605,7 @@ void fused_wide_kernel(const FusedArgs a) {
                 const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
                 sid = slot_ok(v, a.num_slots) ? (int)v : -1;
             }
-            m_pos = pos; m_len = len; m_seq = seq; m_slot = sid;
+            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
         }
     }
 
@@ -608,13 +635,11 @@ void fused_wide_kernel(const FusedArgs a) {
     }
     auto aslot = [&](auto u_c) -> uint8_t* {
         constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else if constexpr (u == 2) return ra2;
-        else return ra3;
+        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else return ra2;
     };
     auto bslot = [&](auto u_c) -> uint8_t* {
         constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else if constexpr (u == 2) return rb2;
-        else return rb3;
+        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else return rb2;
     };
     auto issue = [&](auto u_c, int kt) {
         uint8_t* sa = aslot(u_c);
@@ -638,9 +663,30 @@ void fused_wide_kernel(const FusedArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+    // Halo rows first (the oldest loads, so the first stage's wait covers
+    // them): (K-1) x D bf16 in 1 KiB pieces, row max(t, 0) for a tile at the
+    // start (its first rows take their history from the initial states).
+    if constexpr (kHalo) {
+        constexpr int kPerRow = kRowBytes / 1024;
+        constexpr int kPieces = (K - 1) * kPerRow;
+#pragma unroll
+        for (int i = 0; i < (kPieces + 7) / 8; ++i) {
+            const int pc = wave + 8 * i;
+            if (pc < kPieces) {
+                const int m = pc / kPerRow;
+                const int64_t hr = row0 - (K - 1) + m < 0 ? 0 : row0 - (K - 1) + m;
+                const rsrc_t hs = row_rsrc(a.x + hr * a.x_stride, (uint32_t)kRowBytes);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hs, (lds_ptr_t)(s_halo + pc * 1024), 16,
+                                                         (uint32_t)((pc % kPerRow) * 1024 + lane * 16), 0, 0, 0);
+            }
+        }
+    }
+    float hacc[KH][2];                                 // partial B, xv of the halo rows (first row half)
+#pragma unroll
+    for (int m = 0; m < KH; ++m) hacc[m][0] = hacc[m][1] = 0.f;
+
     issue(IC<0>{}, 0);
     issue(IC<1>{}, 1);
-    if constexpr (NK > 2) issue(IC<2>{}, 2);
     auto stage = [&](auto kt_c) {
         constexpr int kt = decltype(kt_c)::value;
         constexpr int u = kt % kWStages;
@@ -661,6 +707,17 @@ void fused_wide_kernel(const FusedArgs a) {
 #pragma unroll
             for (int j = 0; j < 3; ++j)
                 fb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_chunk(j * kWNC + wn * 32 + q, c));
+            if constexpr (kHalo) {
+                if (wm == 0) {                         // halo rows: the same k values as this lane's fragments
+#pragma unroll
+                    for (int m = 0; m < K - 1; ++m) {
+                        const bf16x8 xh = *reinterpret_cast<const bf16x8*>(
+                            s_halo + m * kRowBytes + (kt * kFBK + kk * 16 + 8 * hl) * 2);
+                        hacc[m][0] = dot8_bf16(xh, fb[0], hacc[m][0]);
+                        hacc[m][1] = dot8_bf16(xh, fb[2], hacc[m][1]);
+                    }
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -683,18 +740,8 @@ void fused_wide_kernel(const FusedArgs a) {
     // ---------------------------------------------------------------- epilogue
     // As in the kernel above, one 32-row tile i at a time, which keeps the
     // working set beside the 192 accumulator registers small.  Each wave stages
-    // its 128 x 32 outputs in its own 8 KiB of the x slots of the (now idle)
-    // ring; the row map goes to the last W_in slot, the row-half hand-off (bx
-    // of rows 125..127 of the first half, per channel) to the one before.
+    // its 128 x 32 outputs in its own 8 KiB of the (now idle) ring.
     __syncthreads();
-    int* s_pos = reinterpret_cast<int*>(rb3);
-    int* s_len = s_pos + kFBM;
-    int* s_seq = s_len + kFBM;
-    int* s_slot = s_seq + kFBM;
-    float (*s_edge)[32][4] = reinterpret_cast<float (*)[32][4]>(rb2);
-    if (tid < kFBM) {
-        s_pos[tid] = m_pos; s_len[tid] = m_len; s_seq[tid] = m_seq; s_slot[tid] = m_slot;
-    }
     if (wm == 0 && hl == 1) {
 #pragma unroll
         for (int m = 0; m < K - 1; ++m) {
@@ -703,7 +750,7 @@ void fused_wide_kernel(const FusedArgs a) {
         }
     }
     lds_barrier();
-    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : ra3));
+    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : rb0));
     uint16_t* wout = reinterpret_cast<uint16_t*>(region + (wave & 1) * kWRegion);   // [128][32]
     const int lcn = wn * 32 + q;
     const int ch = n0 + lcn;
@@ -719,7 +766,7 @@ void fused_wide_kernel(const FusedArgs a) {
             const int id = lane + 64 * k;
             const int rw = id >> 2, cc = id & 3;
             const int row = rbase + rw;
-            if (row >= K - 1 && s_pos[row] >= 0) {
+            if (row >= kFirstOut && s_pos[row] >= 0) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(wout + rw * 32 + cc * 8);
                 *reinterpret_cast<u32x4*>(dst + (row0 + row) * stride + n0 + wn * 32 + cc * 8) = v;
             }
@@ -743,11 +790,19 @@ void fused_wide_kernel(const FusedArgs a) {
     for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
     const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
     const RowMap rm{s_pos, s_len, s_seq, s_slot};
+    // one sequence holds every computed row (and, with halo rows, those too)
     const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
-    const bool simple = p0 >= 0 && pl == p0 + kFBM - 1 && !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
-    float prev[K > 1 ? K - 1 : 1];                     // the partner's last K-1 rows of the previous quad
+    const bool simple = p0 >= (kHalo ? K - 1 : 0) && pl == p0 + kFBM - 1 &&
+                        !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
+    float prev[KH];                                    // the partner's last K-1 rows of the previous quad
 #pragma unroll
-    for (int m = 0; m < K - 1; ++m) prev[m] = wm == 1 ? s_edge[wn][q][m] : 0.f;
+    for (int m = 0; m < K - 1; ++m) {
+        // first row half: bx of the halo rows, from the two lane halves' partial sums
+        float hb = 0.f;
+        if constexpr (kHalo)
+            hb = (hacc[m][0] + __shfl_xor(hacc[m][0], 32)) * (hacc[m][1] + __shfl_xor(hacc[m][1], 32));
+        prev[m] = wm == 1 ? s_edge[wn][q][m] : hb;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float bx[16];
@@ -778,7 +833,8 @@ void fused_wide_kernel(const FusedArgs a) {
                 float cg[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cg[j] = acc[i][1][4 * g + j];
-                quad_general<K>(a, rm, R0, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
+                quad_general<K>(a, rm, R0, kFirstOut, ch, wk, bv, hx, cg,
+                                [&](int j, float v) { stage_out(i, 4 * g + j, v); });
             }
         }
     }
@@ -811,24 +867,60 @@ static void fused_launch_main(const FusedArgs& a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((fused_prefill_kernel<K, NK>), dim3(blocks), dim3(kFThreads), 0, s, a);
 }
 
-template <int K, int NK>
+template <int K, int NK, bool HALO>
 static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((fused_wide_kernel<K, NK>), dim3(blocks), dim3(kWThreads), 0, s, a);
+    hipLaunchKernelGGL((fused_wide_kernel<K, NK, HALO>), dim3(blocks), dim3(kWThreads), 0, s, a);
+}
+
+// Halo or overlapping wide tiles: the one with the shorter expected span, in
+// rounds of resident workgroups, a halo tile counting kHaloTileCost of an
+// overlapping one (measured on MI355X at T=65536, D=H=2048).  T=4096 and 8192
+// take halo tiles (1 round instead of 2, 2 instead of 3), 65536 overlapping
+// ones.  LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form.
+constexpr double kHaloTileCost = 1.14;
+template <int K>
+static bool fused_use_halo(int64_t total_T, int tiles_n) {
+    if (K == 1) return false;
+    if (const char* e = getenv("LFM2SC_FUSED_HALO")) {
+        if (e[0] == '0') return false;
+        if (e[0] == '1') return true;
+    }
+    static const int resident = [] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_wide_kernel<K, 2048 / kFBK, true>, kWThreads, 0) !=
+                hipSuccess || cus <= 0 || per <= 0) {
+            (void)hipGetLastError();
+            return 256;
+        }
+        return cus * per;
+    }();
+    const int64_t halo = (total_T + kFBM - 1) / kFBM * tiles_n;
+    const int64_t ovl = (total_T + fused_out_rows<K>() - 1) / fused_out_rows<K>() * tiles_n;
+    const double rounds_halo = (double)((halo + resident - 1) / resident) * kHaloTileCost;
+    const double rounds_ovl = (double)((ovl + resident - 1) / resident);
+    return rounds_halo < rounds_ovl;
 }
 
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
-    const int64_t out = fused_out_rows<K>();
-    a.tiles_m = (int)((a.total_T + out - 1) / out);
     const bool wide = a.H % kWNC == 0 && (a.D == 1024 || a.D == 1536 || a.D == 2048);
     a.tiles_n = a.H / (wide ? kWNC : kFNC);
+    const bool halo = wide && fused_use_halo<K>(a.total_T, a.tiles_n);
+    const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows
+    a.tiles_m = (int)((a.total_T + out - 1) / out);
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
     if (wide) {
-        switch (a.D) {
-            case 1024: fused_launch_wide<K, 1024 / kFBK>(a, blocks, s); break;
-            case 1536: fused_launch_wide<K, 1536 / kFBK>(a, blocks, s); break;
-            default: fused_launch_wide<K, 2048 / kFBK>(a, blocks, s); break;
-        }
+        auto go = [&](auto halo_c) {
+            constexpr bool H = decltype(halo_c)::value;
+            switch (a.D) {
+                case 1024: fused_launch_wide<K, 1024 / kFBK, H>(a, blocks, s); break;
+                case 1536: fused_launch_wide<K, 1536 / kFBK, H>(a, blocks, s); break;
+                default: fused_launch_wide<K, 2048 / kFBK, H>(a, blocks, s); break;
+            }
+        };
+        if (halo) go(std::true_type{}); else go(std::false_type{});
     } else {
         switch (a.D) {      // straight-line reductions for the LFM2 hidden sizes
             case 1024: fused_launch_main<K, 1024 / kFBK>(a, blocks, s); break;

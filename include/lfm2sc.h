@@ -258,7 +258,10 @@ const char* lfm2sc_last_error(void);
  * Accuracy: B, C and xv are fp32 sums over D and are not rounded before the
  * conv, so y and the final states carry one bf16 rounding of an fp32 result:
  * within the bf16 tolerance of the exact value, but not bit-equal to running
- * a GEMM into bf16 in_proj and then lfm2sc_prefill_ragged.
+ * a GEMM into bf16 in_proj and then lfm2sc_prefill_ragged.  For H % 128 == 0
+ * and D in {1024, 1536, 2048} the call picks one of two tilings by size (the
+ * fp32 sums, and so the results, may differ by rounding between them); the
+ * environment variable LFM2SC_FUSED_HALO=0 or 1 forces one, for testing.
  */
 int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
                          const void* x, int64_t x_stride, int64_t total_T,

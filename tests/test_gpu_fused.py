@@ -17,6 +17,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 BF = torch.bfloat16
 
+# Wide tiles (H % 128 == 0, D in {1024, 1536, 2048}) come in two forms that the library picks per call by
+# expected span: tiles overlapping by K-1 rows, or tiles with K-1 halo rows.  LFM2SC_FUSED_HALO forces one.
+FORMS = {"overlap": "0", "halo": "1"}
+
+
+@pytest.fixture(params=sorted(FORMS))
+def form(request, monkeypatch):
+    monkeypatch.setenv("LFM2SC_FUSED_HALO", FORMS[request.param])
+    return request.param
+
 
 def _say(msg):
     print(msg, flush=True)
@@ -107,11 +117,11 @@ def test_fused_out_of_range_slots():
         assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
 
 
-def test_fused_lfm2_shape_sampled_channels():
+def test_fused_lfm2_shape_sampled_channels(form):
     """LFM2-1.2B layer shape (H = D = 2048) over 4096 tokens in 3 ragged sequences with a pool; the oracle
     computes 24 sampled channels (channels are independent once in_proj is formed)."""
     lens = [1500, 7, 2589]
-    _say("case: fused H=2048 D=2048 T=4096 ragged, sampled channels")
+    _say(f"case: fused H=2048 D=2048 T=4096 ragged, sampled channels, {form} tiles")
     c = wl.fused_case(513, lens, H=2048, K=3, D=2048, slots=6, bias=True)
     y, io, pool = _run(c, with_io=True)
     chans = torch.tensor([0, 1, 31, 32, 63, 64, 100, 511, 512, 777, 1023, 1024, 1300, 1535, 1536, 1600, 1800,
@@ -150,21 +160,21 @@ def test_fused_deterministic():
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 @pytest.mark.parametrize("H", [128, 256])
-def test_fused_wide_tiles(K, H):
+def test_fused_wide_tiles(K, H, form):
     """Channel counts that are multiples of 128 with D = 1024 run the 8-wave wide tile (256 rows x 128 channels):
     ragged sequences, ones shorter than K, a sequence across several row tiles, rows after the last sequence,
     padded x / y / in_proj rows, a pool and a bias."""
     lens = [37, 1, 0, 300, 5, 2, 1, 2, 3, 600]
-    _say(f"case: fused wide tile K={K} H={H} D=1024 lens={lens} padded, tail rows")
+    _say(f"case: fused wide tile K={K} H={H} D=1024 lens={lens} padded, tail rows, {form} tiles")
     c = wl.fused_case(520 + K + H, lens, H=H, K=K, D=1024, slots=len(lens) + 2, bias=True, x_pad=8, tail_rows=5)
     y, io, pool = _run(c, with_io=True, y_pad=8, io_pad=16)
     _check(c, y, io, pool, f"wide K={K} H={H}")
 
 
 @pytest.mark.parametrize("D", [1536, 2048])
-def test_fused_wide_other_depths(D):
+def test_fused_wide_other_depths(D, form):
     """The wide tile's straight-line reductions for the other LFM2 hidden sizes, no pool."""
-    _say(f"case: fused wide tile D={D} H=128 one sequence")
+    _say(f"case: fused wide tile D={D} H=128 one sequence, {form} tiles")
     c = wl.fused_case(530 + D, [777], H=128, K=3, D=D)
     y, io, pool = _run(c, with_io=True)
     _check(c, y, io, pool, f"wide D={D}")
@@ -213,3 +223,15 @@ def test_fused_graph_replays_match_eager():
         for name, a, b in zip(("y", "in_proj_out", "pool"), (y, io, g.pool), ref):
             assert_bits(a, b, f"replay {rep}: {name}")
     _check(c, ref[0].cpu(), ref[1].cpu(), ref[2].cpu(), "graph")
+
+
+@pytest.mark.parametrize("K", [2, 3, 4])
+def test_fused_wide_tile_boundaries(K, form):
+    """Tile boundaries in both forms (halo tiles start at multiples of 256 and take the history of their first
+    K-1 rows from the halo rows): sequences that end exactly at a 256-row boundary, one row before it, and a
+    2-token sequence across it (its second token is row 0 of a halo tile, its first is a halo row)."""
+    lens = [256, 255, 2, 254, 1, 300]
+    _say(f"case: fused wide tile boundaries K={K} lens={lens} H=128 D=1024 pool, {form} tiles")
+    c = wl.fused_case(550 + K, lens, H=128, K=K, D=1024, slots=len(lens) + 1, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    _check(c, y, io, pool, f"boundaries K={K}")
