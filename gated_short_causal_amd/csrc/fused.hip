@@ -510,31 +510,53 @@ void fused_prefill_kernel(const FusedArgs a) {
 }
 
 // ---------------------------------------------------------------- wide tiles
-// The tile above fetches 28 KiB per stage for its MFMA work; on MI355X its
-// loop waits on the vector-memory data path (L2 -> CU), which hardware
-// counters show busy ~80% of the time.  Wide tiles cover 128 channels with 8
-// waves (two per SIMD), each wave still 128 rows x 32 channels, so a stage
-// moves 40 KiB for twice the MFMA work (1.4x less data per FLOP).  Used when
-// H % 128 == 0 and D is one of the unrolled hidden sizes.
+// The tile above fetches 28 KiB per 32-deep stage for its MFMA work; on
+// MI355X its loop waits on the vector-memory data path (L2 -> CU), which
+// hardware counters show busy ~80% of the time.  Wide tiles cover 128
+// channels with 8 waves (two per SIMD), each wave still 128 rows x 32
+// channels, so a stage moves 1.4x fewer bytes per FLOP.  Used when H % 128 ==
+// 0 and D is one of the unrolled hidden sizes.
 //
-// Two forms (HALO).  Without, consecutive tiles overlap by K-1 rows as above.
-// With, a tile outputs all 256 of its rows, so T = 4096 fills exactly one
-// round of 256 CUs instead of spilling 16 tiles into a second; the conv
+// Two forms (HALO).  Without, consecutive tiles overlap by K-1 rows as above;
+// the reduction runs in 64-deep stages through a 2-slot ring that fills the
+// whole 160 KiB of LDS (each staged row is then a whole 128-byte line, and a
+// tile meets half as many stage barriers as with 32-deep stages: ~4% faster).
+// With HALO, a tile outputs all 256 of its rows, so T = 4096 fills exactly
+// one round of 256 CUs instead of spilling 16 tiles into a second; the conv
 // history of its first K-1 rows is bx of the K-1 x rows just before it ("halo
 // rows"): they are staged in LDS once per tile, and the waves of the first row
 // half form their B and xv with bf16 dot products against the W_in fragments
 // they already hold for the MFMAs, stage by stage (fp32 accumulation, no extra
-// W_in traffic).  That work makes a tile ~14% slower on MI355X, so the
-// launcher takes the halo form only when it saves enough rounds of tiles.
+// W_in traffic).  The halo rows need LDS, so this form keeps 32-deep stages in
+// a 3-slot ring; with the dot products a tile is ~14% slower on MI355X, and
+// the launcher takes the halo form only when it saves enough rounds of tiles.
 constexpr int kWNC = 128;                          // channels per wide tile
 constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
-constexpr int kWStages = 3;                        // ring depth: 2 stages in flight ahead of the one in use
-constexpr int kWStageA = kFBM * kFRowBytes;        // 16 KiB of x rows
-constexpr int kWStageB = 3 * kWNC * kFRowBytes;    // 24 KiB of W_in rows
-constexpr int kWDmaA = kFBM / 16 / 8;              // 2 blocks of 16 x rows per wave
-constexpr int kWDmaB = 3 * kWNC / 16 / 8;          // 3 blocks of 16 W_in rows per wave
-constexpr int kWVm = kWDmaA + kWDmaB;
 constexpr int kWRegion = 128 * 32 * 2;             // one wave's bf16 output block: 128 rows x 32 channels
+
+// Stage geometry for a reduction depth of BK per stage.  One global->LDS
+// instruction moves 64 lanes x 16 B = 1 KiB = kRowsPerDma staged rows.  The
+// swizzle places the 16-byte chunks of consecutive rows so that the 16 lanes
+// of a ds_read_b128 quarter (16 consecutive rows, one chunk) hit all 64 banks
+// once: rows 4 apart (64-byte rows) or 2 apart (128-byte rows) rotate the
+// chunk position.
+template <int BK>
+struct WideStage {
+    static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
+    static constexpr int kRowB = 2 * BK;                        // one staged row: BK bf16
+    static constexpr int kChunks = kRowB / 16;
+    static constexpr int kRowsPerDma = 1024 / kRowB;
+    static constexpr int kDmaA = kFBM / kRowsPerDma / 8;        // x blocks per wave per stage
+    static constexpr int kDmaB = 3 * kWNC / kRowsPerDma / 8;    // W_in blocks per wave per stage
+    static constexpr int kVm = kDmaA + kDmaB;
+    static constexpr int kStageA = kFBM * kRowB;
+    static constexpr int kStageB = 3 * kWNC * kRowB;
+    static constexpr int kMfma = BK / 16 * 12;                  // MFMAs per wave per stage
+    __device__ static int rot(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+    __device__ static uint32_t chunk(int r, int c) { return (uint32_t)r * kRowB + (uint32_t)((c ^ rot(r)) << 4); }
+    // global byte offset, within its staged row r, of the chunk that lane `lane` writes
+    __device__ static uint32_t dma_chunk(int lane, int r) { return (uint32_t)(((lane % kChunks) ^ rot(r)) << 4); }
+};
 
 template <int KT, int NK, typename F>
 __device__ __forceinline__ void unroll_stages(F& f) {
@@ -544,21 +566,44 @@ __device__ __forceinline__ void unroll_stages(F& f) {
     }
 }
 
-template <int K, int NK, bool HALO>
-__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fused_wide_kernel(const FusedArgs a) {
-    static_assert(NK >= 2, "at least two stages");
+// LDS of one wide tile: the ring slots (separate arrays, so that the compiler
+// sees that a refill never touches the slot being read), the halo rows, the
+// row map [4][kFBM] (position, length, sequence, slot) and the row-half
+// hand-off [4][32][4] (bx of rows 125..127 of the first half, per channel).
+struct WideLds {
+    uint8_t* ra[3];
+    uint8_t* rb[3];
+    uint8_t* halo;
+    int* map;
+    float* edge;
+};
+
+// Stage loads of a wide tile: the wave's x blocks and W_in blocks, global ->
+// LDS slot (sa, sb); xoff / woff are the lanes' byte offsets in stage 0.
+template <class S>
+__device__ __forceinline__ void wide_issue(rsrc_t xr, rsrc_t wr, uint8_t* sa, uint8_t* sb, const uint32_t* xoff,
+                                           const uint32_t* woff, int wave, uint32_t ko) {
+#pragma unroll
+    for (int i = 0; i < S::kDmaA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(sa + (wave + 8 * i) * 1024), 16, xoff[i] + ko, 0, 0,
+                                                 0);
+#pragma unroll
+    for (int i = 0; i < S::kDmaB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(sb + (wave + 8 * i) * 1024), 16, woff[i] + ko, 0, 0,
+                                                 0);
+}
+
+template <int K, int D, bool HALO, int BK, int NSLOT>
+__device__ __forceinline__ void wide_tile(const FusedArgs& a, const WideLds& L) {
+    using S = WideStage<BK>;
+    constexpr int NK = D / BK;                         // stages
+    static_assert(NK >= NSLOT && NSLOT >= 2, "at least a full ring of stages");
     constexpr int KH = K > 1 ? K - 1 : 1;
-    constexpr int kRowBytes = NK * kFRowBytes;         // one x row: D bf16
-    constexpr bool kHalo = HALO && K > 1;
-    constexpr int kFirstOut = kHalo ? 0 : K - 1;       // rows before it are history, not outputs
-    __shared__ __attribute__((aligned(16))) uint8_t ra0[kWStageA], ra1[kWStageA], ra2[kWStageA];
-    __shared__ __attribute__((aligned(16))) uint8_t rb0[kWStageB], rb1[kWStageB], rb2[kWStageB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_halo[kHalo ? KH * kRowBytes : 16];   // x of the halo rows
-    __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
-    __shared__ int s_len[kFBM], s_seq[kFBM];
-    __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
-    __shared__ float s_edge[4][32][4];           // bx of rows 125..127 per channel group (the second half's history)
+    constexpr int kRowBytes = D * 2;                   // one x row
+    constexpr int kFirstOut = HALO ? 0 : K - 1;        // rows before it are history, not outputs
+    // Without halo rows the ring fills the LDS: the row map waits in registers
+    // (threads 0..255, one row each) and moves into the idle ring afterwards.
+    constexpr bool kMapLate = !HALO;
 
     const int lin = xcd_tile(blockIdx.x, gridDim.x);
     if (lin >= a.tiles_m * a.tiles_n) return;
@@ -571,11 +616,16 @@ void fused_wide_kernel(const FusedArgs a) {
     const int wm = wave >> 2, wn = wave & 3;
     const int H = a.H;
     const int64_t T = a.total_T;
-    const int64_t row0 = kHalo ? (int64_t)mt * kFBM : (int64_t)mt * fused_out_rows<K>() - (K - 1);
+    const int64_t row0 = HALO ? (int64_t)mt * kFBM : (int64_t)mt * fused_out_rows<K>() - (K - 1);
     const int n0 = nt * kWNC;
+    int* s_pos = L.map;
+    int* s_len = L.map + kFBM;
+    int* s_seq = L.map + 2 * kFBM;
+    int* s_slot = L.map + 3 * kFBM;
 
     // row -> (sequence, position, length, slot) map, before any load of the
     // reduction (as in the kernel above)
+    int m_pos = -1, m_len = 0, m_seq = 0, m_slot = -1;
     {
         const int64_t tf = row0 < 0 ? 0 : row0;
         int lo = 0, hi = a.N;
@@ -605,7 +655,11 @@ void fused_wide_kernel(const FusedArgs a) {
                 const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
                 sid = slot_ok(v, a.num_slots) ? (int)v : -1;
             }
-            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
+            if constexpr (kMapLate) {
+                m_pos = pos; m_len = len; m_seq = seq; m_slot = sid;
+            } else {
+                s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
+            }
         }
     }
 
@@ -618,41 +672,23 @@ void fused_wide_kernel(const FusedArgs a) {
     const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((vhi - vlo) * a.x_stride * 2));
     const rsrc_t xr = row_rsrc(a.x + vlo * a.x_stride, xbytes);
     const rsrc_t wr = row_rsrc(a.W, (uint32_t)((int64_t)3 * H * a.D * 2));
-    const int brow = lane >> 2;
-    const uint32_t bchunk = (uint32_t)(((lane & 3) ^ ((brow >> 2) & 3)) << 4);
-    uint32_t xoff[kWDmaA], woff[kWDmaB];
+    const int brow = lane / S::kChunks;                // row within a block of kRowsPerDma
+    uint32_t xoff[S::kDmaA], woff[S::kDmaB];
 #pragma unroll
-    for (int i = 0; i < kWDmaA; ++i) {
-        int64_t t = row0 + (wave + 8 * i) * 16 + brow;
+    for (int i = 0; i < S::kDmaA; ++i) {
+        const int r = (wave + 8 * i) * S::kRowsPerDma + brow;
+        int64_t t = row0 + r;
         t = t < vlo ? vlo : (t >= vhi ? vhi - 1 : t);
-        xoff[i] = (uint32_t)((t - vlo) * a.x_stride * 2) + bchunk;
+        xoff[i] = (uint32_t)((t - vlo) * a.x_stride * 2) + S::dma_chunk(lane, r);
     }
 #pragma unroll
-    for (int i = 0; i < kWDmaB; ++i) {
-        const int n = (wave + 8 * i) * 16 + brow;      // staged W_in row: part n / 128, channel n % 128
+    for (int i = 0; i < S::kDmaB; ++i) {
+        const int n = (wave + 8 * i) * S::kRowsPerDma + brow;   // staged W_in row: part n / 128, channel n % 128
         const int chn = n0 + n % kWNC;                 // H % 128 == 0: every channel of the tile exists
-        woff[i] = (uint32_t)(((int64_t)(n / kWNC) * H + chn) * a.D * 2) + bchunk;
+        woff[i] = (uint32_t)(((int64_t)(n / kWNC) * H + chn) * a.D * 2) + S::dma_chunk(lane, n);
     }
-    auto aslot = [&](auto u_c) -> uint8_t* {
-        constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return ra0; else if constexpr (u == 1) return ra1; else return ra2;
-    };
-    auto bslot = [&](auto u_c) -> uint8_t* {
-        constexpr int u = decltype(u_c)::value;
-        if constexpr (u == 0) return rb0; else if constexpr (u == 1) return rb1; else return rb2;
-    };
-    auto issue = [&](auto u_c, int kt) {
-        uint8_t* sa = aslot(u_c);
-        uint8_t* sb = bslot(u_c);
-        const uint32_t ko = (uint32_t)kt * kFRowBytes;
-#pragma unroll
-        for (int i = 0; i < kWDmaA; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(sa + (wave + 8 * i) * 1024), 16, xoff[i] + ko,
-                                                     0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kWDmaB; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(sb + (wave + 8 * i) * 1024), 16, woff[i] + ko,
-                                                     0, 0, 0);
+    auto issue = [&](uint8_t* sa, uint8_t* sb, int kt) {     // stage kt's loads into ring slot (sa, sb)
+        wide_issue<S>(xr, wr, sa, sb, xoff, woff, wave, (uint32_t)kt * S::kRowB);
     };
 
     f32x16 acc[4][3];
@@ -666,7 +702,7 @@ void fused_wide_kernel(const FusedArgs a) {
     // Halo rows first (the oldest loads, so the first stage's wait covers
     // them): (K-1) x D bf16 in 1 KiB pieces, row max(t, 0) for a tile at the
     // start (its first rows take their history from the initial states).
-    if constexpr (kHalo) {
+    if constexpr (HALO) {
         constexpr int kPerRow = kRowBytes / 1024;
         constexpr int kPieces = (K - 1) * kPerRow;
 #pragma unroll
@@ -676,7 +712,7 @@ void fused_wide_kernel(const FusedArgs a) {
                 const int m = pc / kPerRow;
                 const int64_t hr = row0 - (K - 1) + m < 0 ? 0 : row0 - (K - 1) + m;
                 const rsrc_t hs = row_rsrc(a.x + hr * a.x_stride, (uint32_t)kRowBytes);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(hs, (lds_ptr_t)(s_halo + pc * 1024), 16,
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(hs, (lds_ptr_t)(L.halo + pc * 1024), 16,
                                                          (uint32_t)((pc % kPerRow) * 1024 + lane * 16), 0, 0, 0);
             }
         }
@@ -685,34 +721,36 @@ void fused_wide_kernel(const FusedArgs a) {
 #pragma unroll
     for (int m = 0; m < KH; ++m) hacc[m][0] = hacc[m][1] = 0.f;
 
-    issue(IC<0>{}, 0);
-    issue(IC<1>{}, 1);
+    issue(L.ra[0], L.rb[0], 0);                        // the first NSLOT - 1 stages
+    if constexpr (NSLOT > 2) issue(L.ra[1], L.rb[1], 1);
+    static_assert(NSLOT <= 3, "prologue issues at most two stages");
     auto stage = [&](auto kt_c) {
         constexpr int kt = decltype(kt_c)::value;
-        constexpr int u = kt % kWStages;
-        constexpr int later = NK - 1 - kt < kWStages - 2 ? NK - 1 - kt : kWStages - 2;   // stages after kt in flight
+        constexpr int u = kt % NSLOT;
+        constexpr int later = NK - 1 - kt < NSLOT - 2 ? NK - 1 - kt : NSLOT - 2;   // stages after kt in flight
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<later * kWVm>();
+        wait_vm<later * S::kVm>();
         stage_barrier();
-        if constexpr (kt + kWStages - 1 < NK) issue(IC<(kt + kWStages - 1) % kWStages>{}, kt + kWStages - 1);
-        const uint8_t* sa = aslot(IC<u>{});
-        const uint8_t* sb = bslot(IC<u>{});
+        if constexpr (kt + NSLOT - 1 < NK)
+            issue(L.ra[(kt + NSLOT - 1) % NSLOT], L.rb[(kt + NSLOT - 1) % NSLOT], kt + NSLOT - 1);
+        const uint8_t* sa = L.ra[u];
+        const uint8_t* sb = L.rb[u];
 #pragma unroll
-        for (int kk = 0; kk < kFBK / 16; ++kk) {
+        for (int kk = 0; kk < BK / 16; ++kk) {
             const int c = kk * 2 + hl;
             bf16x8 fa[4], fb[3];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const bf16x8*>(sa + lds_chunk(wm * 128 + i * 32 + q, c));
+                fa[i] = *reinterpret_cast<const bf16x8*>(sa + S::chunk(wm * 128 + i * 32 + q, c));
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_chunk(j * kWNC + wn * 32 + q, c));
-            if constexpr (kHalo) {
+                fb[j] = *reinterpret_cast<const bf16x8*>(sb + S::chunk(j * kWNC + wn * 32 + q, c));
+            if constexpr (HALO) {
                 if (wm == 0) {                         // halo rows: the same k values as this lane's fragments
 #pragma unroll
                     for (int m = 0; m < K - 1; ++m) {
                         const bf16x8 xh = *reinterpret_cast<const bf16x8*>(
-                            s_halo + m * kRowBytes + (kt * kFBK + kk * 16 + 8 * hl) * 2);
+                            L.halo + m * kRowBytes + (kt * BK + kk * 16 + 8 * hl) * 2);
                         hacc[m][0] = dot8_bf16(xh, fb[0], hacc[m][0]);
                         hacc[m][1] = dot8_bf16(xh, fb[2], hacc[m][1]);
                     }
@@ -724,13 +762,13 @@ void fused_wide_kernel(const FusedArgs a) {
                 for (int j = 0; j < 3; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
         }
-        if constexpr (kt + kWStages - 1 < NK) {
-            // refill loads one per 5 MFMAs across the stage: issued in a burst
-            // they stall the wave on a full address queue (~3% slower)
+        if constexpr (kt + NSLOT - 1 < NK) {
+            // the refill loads spread over the stage's MFMAs: issued in a burst
+            // they stall the wave on a full address queue (2-4% slower)
 #pragma unroll
-            for (int g = 0; g < kWVm; ++g) {
+            for (int g = 0; g < S::kVm; ++g) {
                 __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, S::kMfma / S::kVm, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -740,8 +778,15 @@ void fused_wide_kernel(const FusedArgs a) {
     // ---------------------------------------------------------------- epilogue
     // As in the kernel above, one 32-row tile i at a time, which keeps the
     // working set beside the 192 accumulator registers small.  Each wave stages
-    // its 128 x 32 outputs in its own 8 KiB of the (now idle) ring.
+    // its 128 x 32 outputs in its own 8 KiB of the x slots of the (now idle) ring
+    // (and, with three 16 KiB slots, of the first W_in slot).
     __syncthreads();
+    if constexpr (kMapLate) {
+        if (tid < kFBM) {
+            s_pos[tid] = m_pos; s_len[tid] = m_len; s_seq[tid] = m_seq; s_slot[tid] = m_slot;
+        }
+    }
+    float (*s_edge)[32][4] = reinterpret_cast<float (*)[32][4]>(L.edge);
     if (wm == 0 && hl == 1) {
 #pragma unroll
         for (int m = 0; m < K - 1; ++m) {
@@ -750,8 +795,15 @@ void fused_wide_kernel(const FusedArgs a) {
         }
     }
     lds_barrier();
-    uint8_t* region = wave < 2 ? ra0 : (wave < 4 ? ra1 : (wave < 6 ? ra2 : rb0));
-    uint16_t* wout = reinterpret_cast<uint16_t*>(region + (wave & 1) * kWRegion);   // [128][32]
+    uint8_t* region;
+    if constexpr (NSLOT == 2) {                        // 32 KiB x slots: four waves each
+        static_assert(S::kStageA == 4 * kWRegion, "x slot holds four output blocks");
+        region = (wave < 4 ? L.ra[0] : L.ra[1]) + (wave & 3) * kWRegion;
+    } else {                                           // 16 KiB x slots: two waves each, the last two in rb[0]
+        static_assert(S::kStageA == 2 * kWRegion && NSLOT == 3, "x slot holds two output blocks");
+        region = (wave < 2 ? L.ra[0] : (wave < 4 ? L.ra[1] : (wave < 6 ? L.ra[2] : L.rb[0]))) + (wave & 1) * kWRegion;
+    }
+    uint16_t* wout = reinterpret_cast<uint16_t*>(region);   // [128][32]
     const int lcn = wn * 32 + q;
     const int ch = n0 + lcn;
     const int rbase = wm * 128;
@@ -792,14 +844,14 @@ void fused_wide_kernel(const FusedArgs a) {
     const RowMap rm{s_pos, s_len, s_seq, s_slot};
     // one sequence holds every computed row (and, with halo rows, those too)
     const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
-    const bool simple = p0 >= (kHalo ? K - 1 : 0) && pl == p0 + kFBM - 1 &&
+    const bool simple = p0 >= (HALO ? K - 1 : 0) && pl == p0 + kFBM - 1 &&
                         !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
     float prev[KH];                                    // the partner's last K-1 rows of the previous quad
 #pragma unroll
     for (int m = 0; m < K - 1; ++m) {
         // first row half: bx of the halo rows, from the two lane halves' partial sums
         float hb = 0.f;
-        if constexpr (kHalo)
+        if constexpr (HALO)
             hb = (hacc[m][0] + __shfl_xor(hacc[m][0], 32)) * (hacc[m][1] + __shfl_xor(hacc[m][1], 32));
         prev[m] = wm == 1 ? s_edge[wn][q][m] : hb;
     }
@@ -810,7 +862,7 @@ void fused_wide_kernel(const FusedArgs a) {
         for (int r = 0; r < 16; ++r) bx[r] = acc[i][0][r] * acc[i][2][r];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            float tl[K > 1 ? K - 1 : 1];
+            float tl[KH];
 #pragma unroll
             for (int m = 0; m < K - 1; ++m) tl[m] = __shfl_xor(bx[4 * g + 4 - (K - 1) + m], 32);
             float hx[K - 1 + 4];
@@ -841,6 +893,32 @@ void fused_wide_kernel(const FusedArgs a) {
     flush(a.y, a.y_stride);
 }
 
+// The wide tile's kernel: its LDS arrays per form (the halo form's 32-deep
+// 3-slot ring plus halo rows, row map and hand-off; or the 64-deep 2-slot
+// ring alone, exactly 160 KiB, the row map and hand-off going into its second
+// W_in slot after the reduction).
+template <int K, int D, bool HALO>
+__global__ __launch_bounds__(kWThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fused_wide_kernel(const FusedArgs a) {
+    if constexpr (HALO && K > 1) {
+        using S = WideStage<32>;
+        __shared__ __attribute__((aligned(16))) uint8_t ra0[S::kStageA], ra1[S::kStageA], ra2[S::kStageA];
+        __shared__ __attribute__((aligned(16))) uint8_t rb0[S::kStageB], rb1[S::kStageB], rb2[S::kStageB];
+        __shared__ __attribute__((aligned(16))) uint8_t halo[(K - 1) * D * 2];
+        __shared__ __attribute__((aligned(16))) int map[4 * kFBM];
+        __shared__ __attribute__((aligned(16))) float edge[4 * 32 * 4];
+        wide_tile<K, D, true, 32, 3>(a, WideLds{{ra0, ra1, ra2}, {rb0, rb1, rb2}, halo, map, edge});
+    } else {
+        using S = WideStage<64>;
+        static_assert(2 * (S::kStageA + S::kStageB) == 160 * 1024, "the ring fills the LDS");
+        __shared__ __attribute__((aligned(16))) uint8_t ra0[S::kStageA], ra1[S::kStageA];
+        __shared__ __attribute__((aligned(16))) uint8_t rb0[S::kStageB], rb1[S::kStageB];
+        wide_tile<K, D, false, 64, 2>(a, WideLds{{ra0, ra1, nullptr}, {rb0, rb1, nullptr}, nullptr,
+                                                reinterpret_cast<int*>(rb1),
+                                                reinterpret_cast<float*>(rb1 + 4 * kFBM * sizeof(int))});
+    }
+}
+
 // Installs the staged final states: slot_idx[i] <- fin[i] for every sequence
 // with at least one token (an empty sequence leaves its slot as it was).
 __global__ __launch_bounds__(kSmallBlock) void fused_state_commit_kernel(const FusedArgs a, int K) {
@@ -867,9 +945,9 @@ static void fused_launch_main(const FusedArgs& a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((fused_prefill_kernel<K, NK>), dim3(blocks), dim3(kFThreads), 0, s, a);
 }
 
-template <int K, int NK, bool HALO>
+template <int K, int D, bool HALO>
 static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL((fused_wide_kernel<K, NK, HALO>), dim3(blocks), dim3(kWThreads), 0, s, a);
+    hipLaunchKernelGGL((fused_wide_kernel<K, D, HALO>), dim3(blocks), dim3(kWThreads), 0, s, a);
 }
 
 // Halo or overlapping wide tiles: the one with the shorter expected span, in
@@ -889,7 +967,7 @@ static bool fused_use_halo(int64_t total_T, int tiles_n) {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_wide_kernel<K, 2048 / kFBK, true>, kWThreads, 0) !=
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_wide_kernel<K, 2048, true>, kWThreads, 0) !=
                 hipSuccess || cus <= 0 || per <= 0) {
             (void)hipGetLastError();
             return 256;
@@ -915,9 +993,9 @@ static hipError_t fused_k(FusedArgs a, hipStream_t s) {
         auto go = [&](auto halo_c) {
             constexpr bool H = decltype(halo_c)::value;
             switch (a.D) {
-                case 1024: fused_launch_wide<K, 1024 / kFBK, H>(a, blocks, s); break;
-                case 1536: fused_launch_wide<K, 1536 / kFBK, H>(a, blocks, s); break;
-                default: fused_launch_wide<K, 2048 / kFBK, H>(a, blocks, s); break;
+                case 1024: fused_launch_wide<K, 1024, H>(a, blocks, s); break;
+                case 1536: fused_launch_wide<K, 1536, H>(a, blocks, s); break;
+                default: fused_launch_wide<K, 2048, H>(a, blocks, s); break;
             }
         };
         if (halo) go(std::true_type{}); else go(std::false_type{});
