@@ -528,8 +528,9 @@ void fused_prefill_kernel(const FusedArgs a) {
 // half form their B and xv with bf16 dot products against the W_in fragments
 // they already hold for the MFMAs, stage by stage (fp32 accumulation, no extra
 // W_in traffic).  The halo rows need LDS, so this form keeps 32-deep stages in
-// a 3-slot ring; with the dot products a tile is ~14% slower on MI355X, and
-// the launcher takes the halo form only when it saves enough rounds of tiles.
+// a 3-slot ring; with those and the dot products a tile is ~21% slower on
+// MI355X, and the launcher takes the halo form only when it saves enough
+// rounds of tiles.
 constexpr int kWNC = 128;                          // channels per wide tile
 constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
 constexpr int kWRegion = 128 * 32 * 2;             // one wave's bf16 output block: 128 rows x 32 channels
@@ -952,10 +953,11 @@ static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
 
 // Halo or overlapping wide tiles: the one with the shorter expected span, in
 // rounds of resident workgroups, a halo tile counting kHaloTileCost of an
-// overlapping one (measured on MI355X at T=65536, D=H=2048).  T=4096 and 8192
-// take halo tiles (1 round instead of 2, 2 instead of 3), 65536 overlapping
-// ones.  LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form.
-constexpr double kHaloTileCost = 1.14;
+// overlapping one (measured on MI355X, D=H=2048: 88-90 us against 73-74 us
+// per round at T=32768 and 65536).  T up to 16384 takes halo tiles (T=4096:
+// 1 round instead of 2, 0.098 against 0.137 ms), larger T overlapping ones.
+// LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form.
+constexpr double kHaloTileCost = 1.21;
 template <int K>
 static bool fused_use_halo(int64_t total_T, int tiles_n) {
     if (K == 1) return false;
