@@ -335,8 +335,11 @@ def fused_measurements(wl_mod, steps):
             ms = graph_time([fused], steps)
             unf = graph_time([gemm], steps) + graph_time([conv], steps)
         else:
-            ms = timed_loop(fused, steps, 3)
-            unf = timed_loop(gemm, steps, 3) + timed_loop(conv, steps, 3)
+            # the inputs were just generated on the host with the GPU idle: warm up long enough for the
+            # long calls to reach their steady rate (the same for both paths)
+            warm = max(10, steps)
+            ms = timed_loop(fused, steps, warm)
+            unf = timed_loop(gemm, steps, warm) + timed_loop(conv, steps, warm)
         flops = 2.0 * T * D * 3 * H
         tf = flops / ms / 1e9
         out[name] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
