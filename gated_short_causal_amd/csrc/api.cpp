@@ -386,8 +386,15 @@ int lfm2sc_conv_update(int dtype, int H, int K, int num_seqs, int L, const void*
     TRY(check_pool(fn, state_pool, num_slots, slot_stride, slot_idx, H, K));
     if (windows != nullptr && !aligned(windows, 16))
         return fail(LFM2SC_ERR_ALIGNMENT, "%s: windows is not 16-byte aligned", fn);
-    const bool vec = bx_stride_h == 1 && out_stride_h == 1 && bx_stride_n % 8 == 0 && bx_stride_t % 8 == 0 &&
-                     out_stride_n % 8 == 0 && out_stride_t % 8 == 0 && aligned(bx, 16) && aligned(out, 16);
+    // channel-contiguous (the transposed view of token-major rows), token-contiguous (a dense [N][H][L]
+    // tensor), or neither
+    const bool chan_vec = bx_stride_h == 1 && out_stride_h == 1 && bx_stride_n % 8 == 0 && bx_stride_t % 8 == 0 &&
+                          out_stride_n % 8 == 0 && out_stride_t % 8 == 0 && aligned(bx, 16) && aligned(out, 16);
+    const bool rows = bx_stride_t == 1 && out_stride_t == 1;
+    const bool rows_vec = rows && L % 8 == 0 && bx_stride_h % 8 == 0 && out_stride_h % 8 == 0 &&
+                          bx_stride_n % 8 == 0 && out_stride_n % 8 == 0 && aligned(bx, 16) && aligned(out, 16);
+    const ConvLayout lay = chan_vec ? ConvLayout::kChannelsVec
+                                    : rows_vec ? ConvLayout::kRowsVec : rows ? ConvLayout::kRows : ConvLayout::kGeneric;
     hipStream_t s = static_cast<hipStream_t>(stream);
     TRY(device_check(fn, s, slot_idx, num_seqs, num_slots, nullptr, 0, nullptr, 0));
     auto fill = [&](auto* tag) {
@@ -401,7 +408,7 @@ int lfm2sc_conv_update(int dtype, int H, int K, int num_seqs, int L, const void*
         a.win = static_cast<E*>(windows);
         a.out = static_cast<E*>(out); a.out_sn = out_stride_n; a.out_sh = out_stride_h; a.out_st = out_stride_t;
         a.H = H;
-        return launched(fn, launch_conv_update<E>(a, K, vec, s));
+        return launched(fn, launch_conv_update<E>(a, K, lay, s));
     };
     if (dtype == LFM2SC_BF16) return fill(static_cast<uint16_t*>(nullptr));
     return fill(static_cast<float*>(nullptr));

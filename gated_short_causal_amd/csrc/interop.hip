@@ -13,11 +13,14 @@
 // (conv_update_step_kernel); in place, one wave walks a sequence's steps, since
 // it both reads and writes the slot.
 //
-// One wave per (sequence, 512 channels), a lane owning 8 channels, as in the
-// verify kernel; up to 8 tokens' inputs are loaded before any is used.  When
-// the channel stride is 1 and the rows are 16-byte aligned (the transposed
-// view of token-major memory), bx and out move as 16-byte vectors; any other
-// strides (e.g. a dense [N][H][L] tensor) take per-element accesses.
+// Three layouts.  Channel stride 1 with 16-byte aligned rows (the transposed
+// view of token-major memory): one wave per (sequence, 512 channels), a lane
+// owning 8 channels as in the verify kernel, bx and out moving as 16-byte
+// vectors.  Token stride 1 (a dense [N][H][L] tensor, SGLang's own layout):
+// one lane per channel walks that channel's L tokens, which are contiguous, so
+// a wave reads and writes the rows of 64 channels back to back
+// (conv_update_rows_kernel).  Any other strides: the first form with
+// per-element accesses.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -175,8 +178,79 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const Con
     store_block<E, K>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
 }
 
+// Token stride 1: one lane per channel, all L steps of the sequence in the
+// lane.  VEC: L, the channel and batch strides are multiples of 8 elements and
+// the bases 16-byte aligned, so a lane's tokens move 8 at a time as 16-byte
+// (bf16) or 32-byte (fp32) vectors.  Both modes: with a tape the pool is only
+// read and every window goes to the tape (adjacent lanes write adjacent
+// windows); in place the lane writes its slot entries back at the end.
+template <typename E, int K, bool VEC>
+__global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const ConvUpdateArgs<E> a) {
+    const int i = blockIdx.x;
+    const int ch = blockIdx.y * kSmallBlock + threadIdx.x;
+    if (ch >= a.H) return;
+    const int64_t slot = a.slot_idx[i];
+    const bool ok = slot_ok(slot, a.num_slots);
+    float w[K], s[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[k] = ld1<E>(a.w + (int64_t)ch * K + k);
+    const float bv = a.bias != nullptr ? ld1<E>(a.bias + ch) : 0.f;
+    E* sp = ok ? a.pool + slot * a.slot_stride + (int64_t)ch * K : nullptr;
+#pragma unroll
+    for (int k = 0; k < K; ++k) s[k] = ok ? ld1<E>(sp + k) : 0.f;
+    const E* xb = a.bx + (int64_t)i * a.bx_sn + (int64_t)ch * a.bx_sh;
+    E* ob = a.out + (int64_t)i * a.out_sn + (int64_t)ch * a.out_sh;
+    for (int t0 = 0; t0 < a.L; t0 += 8) {
+        const int n = a.L - t0 < 8 ? a.L - t0 : 8;
+        float x[8], y[8];
+        if constexpr (VEC) {
+            load_f32x8<E>(xb + t0, x);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = u < n ? ld1<E>(xb + t0 + u) : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (u < n) {
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) s[k] = s[k + 1];
+                s[K - 1] = x[u];
+                float conv = fmaf(w[K - 1], s[K - 1], bv);
+#pragma unroll
+                for (int k = 0; k < K - 1; ++k) conv = fmaf(w[k], s[k], conv);
+                y[u] = conv;
+                if (a.win != nullptr) {
+                    E* wp = a.win + (((int64_t)i * a.L + t0 + u) * a.H + ch) * K;
+#pragma unroll
+                    for (int k = 0; k < K; ++k) st1<E>(wp + k, s[k]);
+                }
+            }
+        }
+        if constexpr (VEC) {
+            store_f32x8<E>(ob + t0, y);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u < n) st1<E>(ob + t0 + u, y[u]);
+        }
+    }
+    if (a.win == nullptr && ok) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) st1<E>(sp + k, s[k]);
+    }
+}
+
 template <typename E, int K>
-static hipError_t conv_update_k(const ConvUpdateArgs<E>& a, bool vec, hipStream_t st) {
+static hipError_t conv_update_k(const ConvUpdateArgs<E>& a, ConvLayout lay, hipStream_t st) {
+    if (lay == ConvLayout::kRows || lay == ConvLayout::kRowsVec) {
+        const dim3 grid(a.N, (a.H + kSmallBlock - 1) / kSmallBlock);
+        if (lay == ConvLayout::kRowsVec)
+            hipLaunchKernelGGL((conv_update_rows_kernel<E, K, true>), grid, dim3(kSmallBlock), 0, st, a);
+        else
+            hipLaunchKernelGGL((conv_update_rows_kernel<E, K, false>), grid, dim3(kSmallBlock), 0, st, a);
+        return hipGetLastError();
+    }
+    const bool vec = lay == ConvLayout::kChannelsVec;
     const int lanes = a.H / kChPerLane;
     const dim3 grid(a.N, (lanes + kSmallBlock - 1) / kSmallBlock);
     if (a.win != nullptr) {
@@ -195,17 +269,17 @@ static hipError_t conv_update_k(const ConvUpdateArgs<E>& a, bool vec, hipStream_
 }
 
 template <typename E>
-hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, bool vec, hipStream_t s) {
+hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, ConvLayout lay, hipStream_t s) {
     switch (K) {
-        case 1: return conv_update_k<E, 1>(a, vec, s);
-        case 2: return conv_update_k<E, 2>(a, vec, s);
-        case 3: return conv_update_k<E, 3>(a, vec, s);
-        case 4: return conv_update_k<E, 4>(a, vec, s);
+        case 1: return conv_update_k<E, 1>(a, lay, s);
+        case 2: return conv_update_k<E, 2>(a, lay, s);
+        case 3: return conv_update_k<E, 3>(a, lay, s);
+        case 4: return conv_update_k<E, 4>(a, lay, s);
     }
     return hipErrorInvalidValue;
 }
 
-template hipError_t launch_conv_update<uint16_t>(const ConvUpdateArgs<uint16_t>&, int, bool, hipStream_t);
-template hipError_t launch_conv_update<float>(const ConvUpdateArgs<float>&, int, bool, hipStream_t);
+template hipError_t launch_conv_update<uint16_t>(const ConvUpdateArgs<uint16_t>&, int, ConvLayout, hipStream_t);
+template hipError_t launch_conv_update<float>(const ConvUpdateArgs<float>&, int, ConvLayout, hipStream_t);
 
 }  // namespace lfm2sc

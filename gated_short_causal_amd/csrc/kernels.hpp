@@ -76,8 +76,11 @@ struct ConvUpdateArgs {
     E* out; int64_t out_sn, out_sh, out_st;
     int H;
 };
-// vec: channel stride 1 and 16-byte aligned rows for both bx and out.
-template <typename E> hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, bool vec, hipStream_t s);
+// Memory layout of bx and out (both): channel stride 1 (with 16-byte aligned
+// rows: Vec), token stride 1 (Vec: L and the channel and batch strides are
+// multiples of 8 elements, bases 16-byte aligned), or anything else.
+enum class ConvLayout { kChannelsVec, kRowsVec, kRows, kGeneric };
+template <typename E> hipError_t launch_conv_update(const ConvUpdateArgs<E>& a, int K, ConvLayout lay, hipStream_t s);
 
 // Fused in_proj GEMM + ShortConv forward (bf16 only).  x [total_T][x_stride]
 // (D used), W [3H][D]; y [total_T][y_stride]; io: optional in_proj output
