@@ -25,7 +25,10 @@
 #define LFM2SC_SUB_MIN 8       // shortest per-wave token window
 #endif
 #ifndef LFM2SC_FWD_U
-#define LFM2SC_FWD_U 12        // token rows of loads in flight per wave (forward)
+#define LFM2SC_FWD_U 4         // token rows of loads in flight per wave (forward, bf16 I/O)
+#endif
+#ifndef LFM2SC_FWD_U_F32
+#define LFM2SC_FWD_U_F32 2     // same for fp32 I/O (twice the bytes per row)
 #endif
 #ifndef LFM2SC_FWD_TW
 #define LFM2SC_FWD_TW 4        // forward workgroup: waves along time (4: 4 consecutive windows of one 512-channel
