@@ -44,15 +44,11 @@
 #include <cstdlib>
 #include <type_traits>
 
-#include "common.hpp"
-#include "kernels.hpp"
+#include "fused_common.hpp"
 
 namespace lfm2sc {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kFBM = 256;              // token rows computed per tile
 constexpr int kFNC = 64;               // channels per tile
 constexpr int kFBK = 32;               // reduction depth per stage
 constexpr int kFStages = 4;            // ring depth: 3 stages in flight ahead of the one in use
@@ -70,11 +66,6 @@ constexpr int kFOutStride = kFNC + 8;
 
 template <int K> constexpr int fused_out_rows() { return kFBM - (K - 1); }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    f32x2 v = {f, 0.f};
-    return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2)) & 0xffffu);
-}
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 // c + sum of the 8 products a[e] * b[e] (bf16 operands, fp32 accumulation)
@@ -93,52 +84,11 @@ __device__ __forceinline__ uint32_t lds_chunk(int r, int c) {
     return (uint32_t)r * kFRowBytes + (uint32_t)((c ^ ((r >> 2) & 3)) << 4);
 }
 
-// s_waitcnt that waits until at most n vector-memory operations are outstanding
-// (expcnt and lgkmcnt left unconstrained).
-template <int n> __device__ __forceinline__ void wait_vm() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
 
-// Workgroup -> (m, n) tile: XCD-contiguous runs of the linear tile order, in
-// groups of kFGroupM row tiles that sweep every channel tile, so the workgroups
-// an XCD runs at once share x rows and W_in rows in its L2.
-constexpr int kFGroupM = 4;
-__device__ __forceinline__ void fused_tile(int lin, int tiles_m, int tiles_n, int& m, int& n) {
-    const int per_group = kFGroupM * tiles_n;
-    const int g = lin / per_group;
-    const int idx = lin - g * per_group;
-    const int gm = min(kFGroupM, tiles_m - g * kFGroupM);
-    m = g * kFGroupM + idx % gm;
-    n = idx / gm;
-}
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Workgroup barrier between reduction stages without __syncthreads' release
-// fence: that fence waits for every outstanding vector-memory operation, i.e.
-// for the loads of the stages still in flight, which would drain the ring at
-// every stage.  It is not needed here: before the barrier each wave has waited
-// (wait_vm) for its own loads of the stage about to be read, and its LDS reads
-// of the slot about to be refilled were consumed by its MFMAs.  The empty asm
-// statements keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
-// Barrier for LDS hand-offs in the epilogue: the wave's LDS accesses complete
-// (lgkmcnt 0), then the workgroup meets; global stores in flight are not waited
-// for (they touch no LDS).
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));   // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
-template <int v> using IC = std::integral_constant<int, v>;
 
 // Per-row sequence data of a tile's epilogue (LDS): position in the sequence
 // (-1 outside every sequence), sequence length and index, and the row's slot
@@ -531,41 +481,9 @@ void fused_prefill_kernel(const FusedArgs a) {
 // a 3-slot ring; with those and the dot products a tile is ~21% slower on
 // MI355X, and the launcher takes the halo form only when it saves enough
 // rounds of tiles.
-constexpr int kWNC = 128;                          // channels per wide tile
 constexpr int kWThreads = 512;                     // 8 waves: 2 row halves x 4 channel groups of 32
 constexpr int kWRegion = 128 * 32 * 2;             // one wave's bf16 output block: 128 rows x 32 channels
 
-// Stage geometry for a reduction depth of BK per stage.  One global->LDS
-// instruction moves 64 lanes x 16 B = 1 KiB = kRowsPerDma staged rows.  The
-// swizzle places the 16-byte chunks of consecutive rows so that the 16 lanes
-// of a ds_read_b128 quarter (16 consecutive rows, one chunk) hit all 64 banks
-// once: rows 4 apart (64-byte rows) or 2 apart (128-byte rows) rotate the
-// chunk position.
-template <int BK>
-struct WideStage {
-    static_assert(BK == 32 || BK == 64, "32- or 64-deep stages");
-    static constexpr int kRowB = 2 * BK;                        // one staged row: BK bf16
-    static constexpr int kChunks = kRowB / 16;
-    static constexpr int kRowsPerDma = 1024 / kRowB;
-    static constexpr int kDmaA = kFBM / kRowsPerDma / 8;        // x blocks per wave per stage
-    static constexpr int kDmaB = 3 * kWNC / kRowsPerDma / 8;    // W_in blocks per wave per stage
-    static constexpr int kVm = kDmaA + kDmaB;
-    static constexpr int kStageA = kFBM * kRowB;
-    static constexpr int kStageB = 3 * kWNC * kRowB;
-    static constexpr int kMfma = BK / 16 * 12;                  // MFMAs per wave per stage
-    __device__ static int rot(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
-    __device__ static uint32_t chunk(int r, int c) { return (uint32_t)r * kRowB + (uint32_t)((c ^ rot(r)) << 4); }
-    // global byte offset, within its staged row r, of the chunk that lane `lane` writes
-    __device__ static uint32_t dma_chunk(int lane, int r) { return (uint32_t)(((lane % kChunks) ^ rot(r)) << 4); }
-};
-
-template <int KT, int NK, typename F>
-__device__ __forceinline__ void unroll_stages(F& f) {
-    if constexpr (KT < NK) {
-        f(IC<KT>{});
-        unroll_stages<KT + 1, NK>(f);
-    }
-}
 
 // LDS of one wide tile: the ring slots (separate arrays, so that the compiler
 // sees that a refill never touches the slot being read), the halo rows, the
@@ -920,6 +838,7 @@ void fused_wide_kernel(const FusedArgs a) {
     }
 }
 
+
 // Installs the staged final states: slot_idx[i] <- fin[i] for every sequence
 // with at least one token (an empty sequence leaves its slot as it was).
 __global__ __launch_bounds__(kSmallBlock) void fused_state_commit_kernel(const FusedArgs a, int K) {
@@ -941,6 +860,16 @@ int64_t fused_tiles(int64_t total_T, int H, int K) {
 
 int fused_depth_multiple() { return kFBK * kFStages; }
 
+// After the tile kernel: installs the final states when a pool is given.
+static hipError_t fused_commit(const FusedArgs& a, int K, hipStream_t s) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.fin == nullptr) return e;
+    const int64_t chunks = (int64_t)a.H * K / 8;
+    hipLaunchKernelGGL(fused_state_commit_kernel, dim3(a.N, (unsigned)((chunks + kSmallBlock - 1) / kSmallBlock)),
+                       dim3(kSmallBlock), 0, s, a, K);
+    return hipGetLastError();
+}
+
 template <int K, int NK>
 static void fused_launch_main(const FusedArgs& a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((fused_prefill_kernel<K, NK>), dim3(blocks), dim3(kFThreads), 0, s, a);
@@ -958,13 +887,12 @@ static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
 // 1 round instead of 2, 0.098 against 0.137 ms), larger T overlapping ones.
 // LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form.
 constexpr double kHaloTileCost = 1.21;
+// A 4-wave tile's cost relative to a wide overlapping tile (1.8 against 2.6 MB
+// staged per tile; used only against split tiles).
+constexpr double kMainTileCost = 0.80;
+// Wide tiles resident on the device at once.
 template <int K>
-static bool fused_use_halo(int64_t total_T, int tiles_n) {
-    if (K == 1) return false;
-    if (const char* e = getenv("LFM2SC_FUSED_HALO")) {
-        if (e[0] == '0') return false;
-        if (e[0] == '1') return true;
-    }
+static int wide_resident() {
     static const int resident = [] {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
@@ -976,6 +904,16 @@ static bool fused_use_halo(int64_t total_T, int tiles_n) {
         }
         return cus * per;
     }();
+    return resident;
+}
+template <int K>
+static bool fused_use_halo(int64_t total_T, int tiles_n) {
+    if (K == 1) return false;
+    if (const char* e = getenv("LFM2SC_FUSED_HALO")) {
+        if (e[0] == '0') return false;
+        if (e[0] == '1') return true;
+    }
+    const int resident = wide_resident<K>();
     const int64_t halo = (total_T + kFBM - 1) / kFBM * tiles_n;
     const int64_t ovl = (total_T + fused_out_rows<K>() - 1) / fused_out_rows<K>() * tiles_n;
     const double rounds_halo = (double)((halo + resident - 1) / resident) * kHaloTileCost;
@@ -983,13 +921,24 @@ static bool fused_use_halo(int64_t total_T, int tiles_n) {
     return rounds_halo < rounds_ovl;
 }
 
+
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
-    const bool wide = a.H % kWNC == 0 && (a.D == 1024 || a.D == 1536 || a.D == 2048);
+    const bool unrolled = a.D == 1024 || a.D == 1536 || a.D == 2048;
+    const bool wide = a.H % kWNC == 0 && unrolled;
     a.tiles_n = a.H / (wide ? kWNC : kFNC);
     const bool halo = wide && fused_use_halo<K>(a.total_T, a.tiles_n);
     const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows
     a.tiles_m = (int)((a.total_T + out - 1) / out);
+    if (unrolled) {   // split tiles when their expected span is shorter (short inputs)
+        const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, res = wide_resident<K>();
+        const double other = (double)((tiles + res - 1) / res) * (wide ? (halo ? kHaloTileCost : 1.0) : kMainTileCost);
+        const int nc = fused_split_choice(a.total_T, a.H, other);
+        if (nc != 0) {
+            const hipError_t e = launch_fused_split(a, K, nc, s);
+            return e != hipSuccess ? e : fused_commit(a, K, s);
+        }
+    }
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
     if (wide) {
         auto go = [&](auto halo_c) {
@@ -1009,12 +958,7 @@ static hipError_t fused_k(FusedArgs a, hipStream_t s) {
             default: fused_launch_main<K, 0>(a, blocks, s); break;
         }
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.fin == nullptr) return e;
-    const int64_t chunks = (int64_t)a.H * K / 8;
-    hipLaunchKernelGGL(fused_state_commit_kernel, dim3(a.N, (unsigned)((chunks + kSmallBlock - 1) / kSmallBlock)),
-                       dim3(kSmallBlock), 0, s, a, K);
-    return hipGetLastError();
+    return fused_commit(a, K, s);
 }
 
 hipError_t launch_fused_prefill(const FusedArgs& a, int K, hipStream_t s) {

@@ -1,0 +1,468 @@
+// fused_split.hip -- split tiles of the fused in_proj + ShortConv forward
+// (bf16 I/O, fp32 accumulation) for inputs too short to fill the chip with the
+// wide tiles of fused.hip.  It computes what those do (MAX Pipelines LFM2
+// article, "ShortConv implementation (LFM2ShortConv)"): in_proj projects x[t]
+// into B | C | xv, bx = B * xv, the K-tap causal conv over [initial state | bx]
+// per sequence, y = C * conv; final states go to the same per-sequence staging
+// block, installed into the slots by fused.hip's second kernel.
+#include <algorithm>
+#include <cstdlib>
+#include <string>
+
+#include "fused_common.hpp"
+
+namespace lfm2sc {
+
+// ---------------------------------------------------------------- split tiles
+// A tile's time is set by the bytes it stages (x rows and W_in rows over all of
+// D), which reach one CU's LDS at a roughly fixed rate on MI355X: a wide tile
+// stages 2.6 MB at D = 2048 (~75 us).  Short inputs fill few tiles (T = 256:
+// 16 wide tiles for 256 CUs; any T up to 4096 one round or less), so their
+// time is that of one tile.  A split tile is 64 rows x NC channels (NC = 64:
+// 1.1 MB at D = 2048; NC = 32: 0.7 MB), and its 4 waves each reduce their own
+// quarter of D: a wave stages its quarter-rows through a private 2-slot LDS
+// ring, reads the next stage's fragments into registers while the matrix cores
+// work on the current one, and meets no other wave until its reduction ends.
+// Every row of a split tile is an output (T = 512 at NC = 64, or T = 256 at
+// NC = 32, is exactly 256 tiles): the conv history of its first K-1 rows is bx
+// of the K-1 x rows before the tile, staged beside the tile's rows, whose B and
+// xv come from one more row tile of MFMAs against the same W_in fragments (the
+// matrix cores are mostly idle in this load-bound loop).  The four partial sums
+// then go through LDS one row tile (32 rows) at a time, added in a fixed order,
+// and each thread runs the conv for one channel and NC/8 consecutive rows
+// straight from them.
+constexpr int kSBM = 64;                       // token rows per split tile (all of them outputs)
+constexpr int kSWaves = 4;                     // each reduces a quarter of D
+constexpr int kSThreads = kSWaves * 64;
+constexpr int kSStageA = kSBM * 64;            // one wave's stage: 64 x rows of 32 bf16 (4 KiB)
+constexpr int kSStageH = 16 * 64;              // and a block of 16 rows for the K-1 halo rows
+constexpr int kSDmaA = kSBM / 16;              // 1 KiB loads of x rows per wave and stage
+constexpr int64_t split_tiles(int64_t total_T, int H, int nc) { return (total_T + kSBM - 1) / kSBM * (H / nc); }
+
+template <int NC>
+struct SplitGeom {
+    static_assert(NC == 32 || NC == 64, "32 or 64 channels");
+    static constexpr int kCT = 3 * NC / 32;    // column tiles: B, C, xv of the NC channels
+    static constexpr int kHT = 2 * NC / 32;    // the halo row tile needs B and xv only
+    static constexpr int kStageB = 3 * NC * 64;
+    static constexpr int kDmaB = 3 * NC / 16;
+    static constexpr int kVm = kSDmaA + 1 + kDmaB;
+    static constexpr int kCols = 3 * NC;       // partial sums per row: B | C | xv
+    static constexpr int kRpt = 32 * NC / kSThreads;    // epilogue rows per thread and row tile
+    // halo column tile h -> column tile: the B tiles, then the xv tiles
+    __device__ static constexpr int halo_tile(int h) { return h < NC / 32 ? h : h + NC / 32; }
+    // Partial sum (row, col) of a [32][kCols] block.  NC = 64: the column of
+    // rows 4..7 mod 8 is XOR-ed with 32, so the two lane halves of a store (rows
+    // 4 apart, same columns) hit different banks; NC = 32: plain.
+    __device__ static int pidx(int row, int col) {
+        if constexpr (NC == 64) return row * kCols + (col ^ (((row >> 2) & 1) << 5));
+        else return row * kCols + col;
+    }
+};
+
+// Sequence of the first token row of a tile (wave-uniform search of cu_seqlens).
+struct TileSeq {
+    int lo;
+    int64_t c0, c1;
+    int slot_lo;
+};
+__device__ __forceinline__ TileSeq tile_first_seq(const FusedArgs& a, int64_t row0) {
+    const int64_t tf = row0 < 0 ? 0 : row0;
+    int lo = 0, hi = a.N;                          // largest s in [0, N) with cu[s] <= tf
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
+    }
+    return TileSeq{lo, a.cu[lo], a.cu[lo + 1], a.pool != nullptr ? a.slot_idx[lo] : -1};
+}
+
+// Row r of a tile of `rows` rows from token row0: position in its sequence (-1
+// outside every sequence), length, sequence, slot (-1 without a pool or out of
+// range).  Arithmetic when the first row's sequence covers the tile, else a
+// per-row search.
+__device__ __forceinline__ void tile_row(const FusedArgs& a, const TileSeq& f, int64_t row0, int rows, int r,
+                                         int& pos, int& len, int& seq, int& sid) {
+    const int64_t tf = row0 < 0 ? 0 : row0;
+    const int64_t t = row0 + r;
+    pos = -1; len = 0; seq = f.lo;
+    if (f.c0 <= tf && f.c1 >= row0 + rows) {
+        if (t >= tf) { pos = (int)(t - f.c0); len = (int)(f.c1 - f.c0); }
+    } else if (t >= 0 && t < a.total_T) {
+        int l2 = 0, h2 = a.N;
+        while (h2 - l2 > 1) {
+            const int mid = (l2 + h2) >> 1;
+            if ((int64_t)a.cu[mid] <= t) l2 = mid; else h2 = mid;
+        }
+        seq = l2;
+        const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
+        if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
+    }
+    sid = -1;
+    if (a.pool != nullptr && pos >= 0) {
+        const int64_t v = seq == f.lo ? f.slot_lo : a.slot_idx[seq];
+        sid = slot_ok(v, a.num_slots) ? (int)v : -1;
+    }
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((63 & 15) | (7 << 4) | (0 << 8) | ((63 >> 4) << 14));
+}
+
+// One wave's stage loads, global -> LDS: its 4 blocks of x rows, the halo block
+// and the W_in blocks.
+template <int NC>
+__device__ __forceinline__ void split_issue(rsrc_t xr, rsrc_t hr, rsrc_t wr, uint8_t* sa, uint8_t* sh, uint8_t* sb,
+                                            const uint32_t* xoff, uint32_t hoff, const uint32_t* woff, uint32_t ko) {
+#pragma unroll
+    for (int i = 0; i < kSDmaA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(sa + i * 1024), 16, xoff[i] + ko, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (lds_ptr_t)sh, 16, hoff + ko, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < SplitGeom<NC>::kDmaB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(sb + i * 1024), 16, woff[i] + ko, 0, 0, 0);
+}
+
+// A stage's MFMA operands: [row tile][k step] of x, [k step] of the halo rows,
+// [column tile][k step] of W_in.
+template <int NC>
+struct SplitFrags {
+    bf16x8 a[2][2];
+    bf16x8 h[2];
+    bf16x8 b[SplitGeom<NC>::kCT][2];
+};
+template <int NC>
+__device__ __forceinline__ void split_read(SplitFrags<NC>& f, const uint8_t* sa, const uint8_t* sh, const uint8_t* sb,
+                                           int q, int hl) {
+    using S = WideStage<32>;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int c = kk * 2 + hl;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) f.a[i][kk] = *reinterpret_cast<const bf16x8*>(sa + S::chunk(i * 32 + q, c));
+        // rows 16..31 of the halo row tile repeat rows 0..15: their sums are never read
+        f.h[kk] = *reinterpret_cast<const bf16x8*>(sh + S::chunk(q & 15, c));
+#pragma unroll
+        for (int j = 0; j < SplitGeom<NC>::kCT; ++j)
+            f.b[j][kk] = *reinterpret_cast<const bf16x8*>(sb + S::chunk(j * 32 + q, c));
+    }
+}
+
+template <int K, int D, int NC>
+__global__ __launch_bounds__(kSThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fused_split_kernel(const FusedArgs a) {
+    using S = WideStage<32>;                           // 64-byte staged rows: its swizzle and chunk map
+    using G = SplitGeom<NC>;
+    constexpr int NKW = D / kSWaves / 32;              // stages per wave
+    static_assert(D % (kSWaves * 32) == 0 && NKW >= 3, "whole stages, at least three per wave");
+    constexpr int KH = K > 1 ? K - 1 : 1;
+    constexpr int CT = G::kCT, HT = G::kHT, RPT = G::kRpt;
+    constexpr int HTK = K > 1 ? HT : 0;                // halo MFMAs per k step (none without history)
+    constexpr int kMf = 2 * (2 * CT + HTK);            // MFMAs per wave and stage
+    static_assert(KH < RPT, "a thread's history rows lie in the group before it");
+    __shared__ __attribute__((aligned(16))) uint8_t sa0[kSWaves * kSStageA], sa1[kSWaves * kSStageA];
+    __shared__ __attribute__((aligned(16))) uint8_t sh0[kSWaves * kSStageH], sh1[kSWaves * kSStageH];
+    __shared__ __attribute__((aligned(16))) uint8_t sb0[kSWaves * G::kStageB], sb1[kSWaves * G::kStageB];
+    __shared__ int s_pos[kSBM], s_len[kSBM], s_seq[kSBM], s_slot[kSBM];
+    __shared__ float s_hpart[kSWaves][KH][2 * NC];     // halo rows' B | xv partial sums per wave
+    __shared__ float s_edge[KH][NC];                   // bx of rows 32-(K-1) .. 31 (the second row tile's history)
+
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    if (lin >= a.tiles_m * a.tiles_n) return;
+    int mt, nt;
+    fused_tile(lin, a.tiles_m, a.tiles_n, mt, nt);
+    const int tid = threadIdx.x;
+    const int wave = wave_id();
+    const int lane = tid & 63;
+    const int q = lane & 31, hl = lane >> 5;
+    const int H = a.H;
+    const int64_t T = a.total_T;
+    const int64_t row0 = (int64_t)mt * kSBM;           // token of row 0 of the tile
+    const int n0 = nt * NC;
+
+    {   // row map, before any load of the reduction (as in the kernels above)
+        const TileSeq f = tile_first_seq(a, row0);
+        if (tid < kSBM) {
+            int pos, len, seq, sid;
+            tile_row(a, f, row0, kSBM, tid, pos, len, seq, sid);
+            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
+        }
+    }
+
+    // ---------------------------------------------------------------- reduction
+    // Wave w reduces k in [w*D/4, (w+1)*D/4).  Staged rows: the tile's x rows
+    // (rows at or past T clamped to a valid row: never outputs, never history
+    // of an output); the halo block, whose rows e < K-1 are x rows row0-(K-1)+e
+    // when those exist (the rest lie outside its descriptor and read as zero
+    // without a memory access); W_in rows (n / NC) * H + n0 + n % NC.
+    const int64_t vhi = (row0 + kSBM < T) ? row0 + kSBM : T;     // > row0 for every launched tile
+    const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((vhi - row0) * a.x_stride * 2));
+    const rsrc_t xr = row_rsrc(a.x + row0 * a.x_stride, xbytes);
+    const int64_t hlo = row0 - (K - 1) < 0 ? 0 : row0 - (K - 1);
+    const uint32_t hbytes = __builtin_amdgcn_readfirstlane((uint32_t)((row0 - hlo) * a.x_stride * 2));
+    const rsrc_t hr = row_rsrc(a.x + hlo * a.x_stride, hbytes);
+    const rsrc_t wr = row_rsrc(a.W, (uint32_t)((int64_t)3 * H * D * 2));
+    const int brow = lane >> 2;
+    const uint32_t kq = (uint32_t)wave * (D / kSWaves) * 2;      // byte offset of the wave's k range
+    uint32_t xoff[kSDmaA], woff[G::kDmaB];
+#pragma unroll
+    for (int i = 0; i < kSDmaA; ++i) {
+        const int r = 16 * i + brow;
+        int64_t t = row0 + r;
+        t = t >= vhi ? vhi - 1 : t;
+        xoff[i] = (uint32_t)((t - row0) * a.x_stride * 2) + kq + S::dma_chunk(lane, r);
+    }
+    uint32_t hoff;
+    {
+        const int64_t t = row0 - (K - 1) + brow;
+        hoff = (brow < K - 1 && t >= hlo) ? (uint32_t)((t - hlo) * a.x_stride * 2) + kq + S::dma_chunk(lane, brow)
+                                          : 0x80000000u;
+    }
+#pragma unroll
+    for (int i = 0; i < G::kDmaB; ++i) {
+        const int n = 16 * i + brow;
+        woff[i] = (uint32_t)(((int64_t)(n / NC) * H + n0 + (n % NC)) * D * 2) + kq + S::dma_chunk(lane, n);
+    }
+    uint8_t* const xa0 = sa0 + wave * kSStageA;
+    uint8_t* const xa1 = sa1 + wave * kSStageA;
+    uint8_t* const ha0 = sh0 + wave * kSStageH;
+    uint8_t* const ha1 = sh1 + wave * kSStageH;
+    uint8_t* const wb0 = sb0 + wave * G::kStageB;
+    uint8_t* const wb1 = sb1 + wave * G::kStageB;
+
+    f32x16 acc[2][CT], acch[HT];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < CT; ++j) acc[i][j][r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < HT; ++j) acch[j][r] = 0.f;
+    }
+    SplitFrags<NC> fr[2];
+    auto mfma = [&](const SplitFrags<NC>& f, int m) {   // MFMA m of a stage, k step major
+        constexpr int per = 2 * CT + HTK;
+        const int kk = m / per, t = m % per;
+        if (t < 2 * CT)
+            acc[t / CT][t % CT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[t / CT][kk], f.b[t % CT][kk],
+                                                                        acc[t / CT][t % CT], 0, 0, 0);
+        else
+            acch[t - 2 * CT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                f.h[kk], f.b[G::halo_tile(t - 2 * CT)][kk], acch[t - 2 * CT], 0, 0, 0);
+    };
+
+    // Stage s computes from fr[s & 1] (read during stage s-1); meanwhile it
+    // reads stage s+1 from its slot into fr[(s+1) & 1], then refills that slot
+    // with stage s+3.  Stages s+1 and s+2 are in flight when it starts.
+    split_issue<NC>(xr, hr, wr, xa0, ha0, wb0, xoff, hoff, woff, 0);
+    split_issue<NC>(xr, hr, wr, xa1, ha1, wb1, xoff, hoff, woff, 64);
+    wait_vm<G::kVm>();
+    split_read<NC>(fr[0], xa0, ha0, wb0, q, hl);
+    wait_lgkm0();
+    split_issue<NC>(xr, hr, wr, xa0, ha0, wb0, xoff, hoff, woff, 2 * 64);
+    auto stage = [&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr int cur = s & 1, nxt = cur ^ 1;
+        constexpr int kLead = 8;                       // MFMAs before the refill: the reads above land meanwhile
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s + 1 < NKW) {
+            wait_vm<(s + 2 < NKW) ? G::kVm : 0>();
+            split_read<NC>(fr[nxt], nxt ? xa1 : xa0, nxt ? ha1 : ha0, nxt ? wb1 : wb0, q, hl);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < kLead; ++m) mfma(fr[cur], m);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s + 3 < NKW) {
+            wait_lgkm0();
+            __builtin_amdgcn_sched_barrier(0);
+            split_issue<NC>(xr, hr, wr, nxt ? xa1 : xa0, nxt ? ha1 : ha0, nxt ? wb1 : wb0, xoff, hoff, woff,
+                            (uint32_t)(s + 3) * 64);
+        }
+#pragma unroll
+        for (int m = kLead; m < kMf; ++m) mfma(fr[cur], m);
+        if constexpr (s + 3 < NKW) {
+            constexpr int per = (kMf - kLead) / G::kVm;        // refill loads spread over the MFMAs
+#pragma unroll
+            for (int m = 0; m < G::kVm; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, per > 0 ? per : 1, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_stages<0, NKW>(stage);
+
+    // ---------------------------------------------------------------- epilogue
+    // Accumulator register r of row tile i, column tile j holds row
+    // i*32 + 8*(r/4) + 4*hl + (r%4), column j*32 + q (columns: B of the NC
+    // channels, then C, then xv); of the halo row tile, registers r < K-1 of the
+    // lanes hl = 0 hold halo rows r.  Partials [32][3NC] fp32 per wave, in the
+    // W_in halves of the ring.
+    if (hl == 0) {
+#pragma unroll
+        for (int j = 0; j < HT; ++j)
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) s_hpart[wave][e][j * 32 + q] = acch[j][e];
+    }
+    lds_barrier();                                     // every wave's reduction is done
+    float* const part0 = reinterpret_cast<float*>(sb0);
+    float* const part1 = part0 + 32 * G::kCols;
+    float* const part2 = reinterpret_cast<float*>(sb1);
+    float* const part3 = part2 + 32 * G::kCols;
+    float* const mine = wave == 0 ? part0 : wave == 1 ? part1 : wave == 2 ? part2 : part3;
+    auto psum = [&](int row, int col) {
+        const int o = G::pidx(row, col);
+        return ((part0[o] + part1[o]) + part2[o]) + part3[o];
+    };
+    const int c = tid % NC;                            // epilogue thread: channel n0 + c,
+    const int grp = tid / NC;                          // rows RPT*grp .. +RPT of each row tile
+    const int ch = n0 + c;
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
+    const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
+
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mine[G::pidx(8 * (r >> 2) + 4 * hl + (r & 3), 32 * j + q)] = acc[p][j][r];
+        lds_barrier();
+        // Initial-state entries the rows need, fetched together first from
+        // addresses chosen without branching (an entry not needed reads the
+        // channel's weight instead).
+        float sv[RPT][KH];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int R = 32 * p + RPT * grp + i;
+            const int pos = s_pos[R], slot = s_slot[R];
+#pragma unroll
+            for (int k = 0; k < KH; ++k) {
+                const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
+                const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
+                                           : a.w + (int64_t)ch * K;
+                sv[i][k] = need ? bf16_val(*src) : 0.f;
+            }
+        }
+        // hb[m]: bx of row RPT*grp - (K-1) + m of this row tile
+        float hb[KH + RPT];
+#pragma unroll
+        for (int m = 0; m < K - 1; ++m) {
+            const int rr = RPT * grp - (K - 1) + m;
+            float v;
+            if (rr >= 0) v = psum(rr, c) * psum(rr, 2 * NC + c);
+            else if (p == 1) v = s_edge[m][c];         // rr < 0 only for grp 0: rows 32-(K-1)+m of row tile 0
+            else                                       // p == 0, grp 0: halo row m
+                v = (((s_hpart[0][m][c] + s_hpart[1][m][c]) + s_hpart[2][m][c]) + s_hpart[3][m][c]) *
+                    (((s_hpart[0][m][NC + c] + s_hpart[1][m][NC + c]) + s_hpart[2][m][NC + c]) + s_hpart[3][m][NC + c]);
+            hb[m] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) hb[K - 1 + i] = psum(RPT * grp + i, c) * psum(RPT * grp + i, 2 * NC + c);
+        if (p == 0 && grp == kSThreads / NC - 1) {
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) s_edge[e][c] = hb[RPT + e];
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int R = 32 * p + RPT * grp + i;      // row of the tile
+            const int pos = s_pos[R];
+            if (pos < 0) continue;                     // no sequence's token
+            const float bxr = hb[K - 1 + i];
+            float h[KH];
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) h[k] = pos < K - 1 - k ? sv[i][k] : hb[i + k];
+            float conv = fmaf(wk[K - 1], bxr, bv);
+#pragma unroll
+            for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], h[k], conv);
+            const int64_t t = row0 + R;
+            const float cg = psum(RPT * grp + i, NC + c);
+            a.y[t * a.y_stride + ch] = bf16_bits(cg * conv);
+            if (a.io != nullptr) {
+                uint16_t* io = a.io + t * a.io_stride + ch;
+                io[0] = bf16_bits(psum(RPT * grp + i, c));
+                io[H] = bf16_bits(cg);
+                io[2 * H] = bf16_bits(psum(RPT * grp + i, 2 * NC + c));
+            }
+            if (a.fin != nullptr && pos == s_len[R] - 1) {
+                uint16_t* f = a.fin + (int64_t)s_seq[R] * H * K + (int64_t)ch * K;
+#pragma unroll
+                for (int e = 0; e < K - 1; ++e) f[e] = bf16_bits(h[e]);
+                f[K - 1] = bf16_bits(bxr);
+            }
+        }
+        if (p == 0) lds_barrier();                     // partials are overwritten next; s_edge written
+    }
+}
+
+template <int K, int D, int NC>
+static void split_launch(const FusedArgs& a, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL((fused_split_kernel<K, D, NC>), dim3(blocks), dim3(kSThreads), 0, s, a);
+}
+
+template <int K, int NC>
+static void split_k(const FusedArgs& a, int blocks, hipStream_t s) {
+    switch (a.D) {
+        case 1024: split_launch<K, 1024, NC>(a, blocks, s); break;
+        case 1536: split_launch<K, 1536, NC>(a, blocks, s); break;
+        default: split_launch<K, 2048, NC>(a, blocks, s); break;
+    }
+}
+
+hipError_t launch_fused_split(FusedArgs a, int K, int nc, hipStream_t s) {
+    a.tiles_n = a.H / nc;
+    a.tiles_m = (int)((a.total_T + kSBM - 1) / kSBM);
+    const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
+    switch (K * 100 + nc) {
+        case 132: split_k<1, 32>(a, blocks, s); break;
+        case 164: split_k<1, 64>(a, blocks, s); break;
+        case 232: split_k<2, 32>(a, blocks, s); break;
+        case 264: split_k<2, 64>(a, blocks, s); break;
+        case 332: split_k<3, 32>(a, blocks, s); break;
+        case 364: split_k<3, 64>(a, blocks, s); break;
+        case 432: split_k<4, 32>(a, blocks, s); break;
+        case 464: split_k<4, 64>(a, blocks, s); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// A split tile's cost relative to a wide overlapping tile, measured on MI355X at
+// D = H = 2048 (it follows the bytes a tile stages: 1.1 MB at 64 channels, 0.7
+// MB at 32, 2.6 MB for the wide tile).
+constexpr double kSplitTileCost64 = 0.45, kSplitTileCost32 = 0.30;
+
+int fused_split_choice(int64_t total_T, int H, double other) {
+    const bool ok64 = H % 64 == 0 && split_tiles(total_T, H, 64) < (1 << 30);
+    const bool ok32 = H % 32 == 0 && split_tiles(total_T, H, 32) < (1 << 30);
+    bool force = false;
+    if (const char* e = getenv("LFM2SC_FUSED_SPLIT")) {
+        const std::string v(e);
+        if (v == "0") return 0;
+        if (v == "64") return ok64 ? 64 : 0;
+        if (v == "32") return ok32 ? 32 : 0;
+        force = v == "1";
+    }
+    static const int resident = [] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, fused_split_kernel<3, 2048, 64>, kSThreads, 0) !=
+                hipSuccess || cus <= 0 || per <= 0) {
+            (void)hipGetLastError();
+            return 256;
+        }
+        return cus * per;
+    }();
+    auto span = [&](int64_t tiles, double cost) { return (double)((tiles + resident - 1) / resident) * cost; };
+    const double s64 = ok64 ? span(split_tiles(total_T, H, 64), kSplitTileCost64) : 1e300;
+    const double s32 = ok32 ? span(split_tiles(total_T, H, 32), kSplitTileCost32) : 1e300;
+    if (!ok64 && !ok32) return 0;
+    const int best = s32 < s64 ? 32 : 64;
+    if (force) return best;
+    return std::min(s32, s64) < other ? best : 0;
+}
+
+}  // namespace lfm2sc

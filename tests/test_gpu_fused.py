@@ -17,14 +17,19 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 BF = torch.bfloat16
 
-# Wide tiles (H % 128 == 0, D in {1024, 1536, 2048}) come in two forms that the library picks per call by
-# expected span: tiles overlapping by K-1 rows, or tiles with K-1 halo rows.  LFM2SC_FUSED_HALO forces one.
-FORMS = {"overlap": "0", "halo": "1"}
+# For D in {1024, 1536, 2048} the library picks a tile form per call by expected span: wide tiles (H % 128 == 0)
+# overlapping by K-1 rows, wide tiles with K-1 halo rows, or split tiles (64 rows x 32 or 64 channels, each of
+# the 4 waves reducing a quarter of D, K-1 halo rows).  LFM2SC_FUSED_SPLIT and LFM2SC_FUSED_HALO force one.
+FORMS = {"overlap": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "0"},
+         "halo": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "1"},
+         "split32": {"LFM2SC_FUSED_SPLIT": "32"},
+         "split64": {"LFM2SC_FUSED_SPLIT": "64"}}
 
 
 @pytest.fixture(params=sorted(FORMS))
 def form(request, monkeypatch):
-    monkeypatch.setenv("LFM2SC_FUSED_HALO", FORMS[request.param])
+    for k, v in FORMS[request.param].items():
+        monkeypatch.setenv(k, v)
     return request.param
 
 
@@ -235,3 +240,38 @@ def test_fused_wide_tile_boundaries(K, form):
     c = wl.fused_case(550 + K, lens, H=128, K=K, D=1024, slots=len(lens) + 1, bias=True)
     y, io, pool = _run(c, with_io=True)
     _check(c, y, io, pool, f"boundaries K={K}")
+
+
+@pytest.mark.parametrize("nc", ["32", "64"])
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("H", [64, 192])
+def test_fused_split_tiles(K, H, nc, monkeypatch):
+    """Split tiles of 32 and 64 channels also serve channel counts that are not multiples of 128.  A split tile
+    starts at a multiple of 64 rows and takes the history of its first K-1 rows from halo rows: sequences that
+    end exactly at such a boundary, one row before and one row after it, a 2-token sequence across it, sequences
+    shorter than K, an empty one, a sequence over several tiles, rows after the last sequence, padded rows, a
+    pool, a bias."""
+    monkeypatch.setenv("LFM2SC_FUSED_SPLIT", nc)
+    lens = [64, 63, 2, 65, 1, 0, 190, 5, 1, 2]
+    _say(f"case: fused split tiles nc={nc} K={K} H={H} D=1024 lens={lens} padded, tail rows")
+    c = wl.fused_case(560 + K + H, lens, H=H, K=K, D=1024, slots=len(lens) + 2, bias=True, x_pad=8, tail_rows=9)
+    y, io, pool = _run(c, with_io=True, y_pad=8, io_pad=16)
+    _check(c, y, io, pool, f"split{nc} K={K} H={H}")
+
+
+def test_fused_one_token_sequences_lfm2_shape():
+    """256 one-token sequences at the LFM2-1.2B layer shape (H = D = 2048) with a pool: every conv history comes
+    from the slots.  The library's own choice of tile form (split tiles for inputs this short); the oracle
+    computes sampled channels."""
+    lens = [1] * 256
+    _say("case: fused 256 one-token sequences H=2048 D=2048 pool, default tile form")
+    c = wl.fused_case(570, lens, H=2048, K=3, D=2048, slots=300, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    chans = torch.tensor([0, 5, 63, 64, 127, 640, 1023, 1024, 1999, 2047])
+    H = c.H
+    rows = torch.cat([chans, chans + H, chans + 2 * H])
+    y_ref, p_ref, ip_ref = oracle.fused_prefill(c.x, c.W_in[rows], c.cu, c.w[chans], c.pool[:, chans, :],
+                                                c.slot_idx, bias=c.bias[chans])
+    assert_close(y[:, chans], y_ref, BF, "y (sampled)")
+    assert_close(io[:, rows], ip_ref, BF, "in_proj_out (sampled)")
+    assert_close(pool[:, chans, :], p_ref, BF, "final states (sampled)")
