@@ -183,40 +183,11 @@ void fused_prefill_kernel(const FusedArgs a) {
     const int64_t row0 = (int64_t)mt * fused_out_rows<K>() - (K - 1);   // token of computed row 0
     const int n0 = nt * kFNC;                                           // first channel of the tile
 
-    // Row -> (sequence, position, length) map of the tile, for the epilogue.  It
-    // is built before any load of the reduction is issued: waiting on a vector
-    // load would also wait on every load issued before it.  The sequence of the
-    // tile's first row comes from a wave-uniform (scalar) search; when that
-    // sequence covers every computed row, the map is arithmetic, otherwise each
-    // row searches cu_seqlens itself.
+    // Row -> (sequence, position, length, slot) map of the tile, for the epilogue.
     {
-        const int64_t tf = row0 < 0 ? 0 : row0;
-        int lo = 0, hi = a.N;                      // largest s in [0, N) with cu[s] <= tf
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
-        }
-        const int64_t c0 = a.cu[lo], c1 = a.cu[lo + 1];
-        const int slot_lo = a.pool != nullptr ? a.slot_idx[lo] : -1;   // loaded beside c0, c1
-        const int64_t t = row0 + tid;
-        int pos = -1, len = 0, seq = lo;
-        if (c0 <= tf && c1 >= row0 + kFBM) {       // one sequence holds rows [tf, row0 + 256)
-            if (t >= tf) { pos = (int)(t - c0); len = (int)(c1 - c0); }
-        } else if (t >= 0 && t < T) {
-            int l2 = 0, h2 = a.N;
-            while (h2 - l2 > 1) {
-                const int mid = (l2 + h2) >> 1;
-                if ((int64_t)a.cu[mid] <= t) l2 = mid; else h2 = mid;
-            }
-            seq = l2;
-            const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
-            if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
-        }
-        int sid = -1;                              // the row's slot, if it has one in range
-        if (a.pool != nullptr && pos >= 0) {
-            const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
-            sid = slot_ok(v, a.num_slots) ? (int)v : -1;
-        }
+        const TileSeq f = tile_first_seq(a, row0);
+        int pos, len, seq, sid;
+        tile_row(a, f, row0, kFBM, tid, pos, len, seq, sid);
         s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
     }
 
@@ -546,34 +517,10 @@ __device__ __forceinline__ void wide_tile(const FusedArgs& a, const WideLds& L) 
     // reduction (as in the kernel above)
     int m_pos = -1, m_len = 0, m_seq = 0, m_slot = -1;
     {
-        const int64_t tf = row0 < 0 ? 0 : row0;
-        int lo = 0, hi = a.N;
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
-        }
-        const int64_t c0 = a.cu[lo], c1 = a.cu[lo + 1];
-        const int slot_lo = a.pool != nullptr ? a.slot_idx[lo] : -1;   // loaded beside c0, c1
+        const TileSeq f = tile_first_seq(a, row0);
         if (tid < kFBM) {
-            const int64_t t = row0 + tid;
-            int pos = -1, len = 0, seq = lo;
-            if (c0 <= tf && c1 >= row0 + kFBM) {
-                if (t >= tf) { pos = (int)(t - c0); len = (int)(c1 - c0); }
-            } else if (t >= 0 && t < T) {
-                int l2 = 0, h2 = a.N;
-                while (h2 - l2 > 1) {
-                    const int mid = (l2 + h2) >> 1;
-                    if ((int64_t)a.cu[mid] <= t) l2 = mid; else h2 = mid;
-                }
-                seq = l2;
-                const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
-                if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
-            }
-            int sid = -1;                              // the row's slot, if it has one in range
-            if (a.pool != nullptr && pos >= 0) {
-                const int64_t v = seq == lo ? slot_lo : a.slot_idx[seq];
-                sid = slot_ok(v, a.num_slots) ? (int)v : -1;
-            }
+            int pos, len, seq, sid;
+            tile_row(a, f, row0, kFBM, tid, pos, len, seq, sid);
             if constexpr (kMapLate) {
                 m_pos = pos; m_len = len; m_seq = seq; m_slot = sid;
             } else {

@@ -103,6 +103,55 @@ __device__ __forceinline__ void unroll_stages(F& f) {
     }
 }
 
+// Row map of a tile, built before any load of its reduction (waiting on a
+// vector load would also wait on every load issued before it).  The sequence
+// of the tile's first row comes from a wave-uniform (scalar) search; when that
+// sequence covers every row of the tile, each row's entry is arithmetic,
+// otherwise each row searches cu_seqlens itself.
+// Sequence of the first token row of a tile (wave-uniform search of cu_seqlens).
+struct TileSeq {
+    int lo;
+    int64_t c0, c1;
+    int slot_lo;
+};
+__device__ __forceinline__ TileSeq tile_first_seq(const FusedArgs& a, int64_t row0) {
+    const int64_t tf = row0 < 0 ? 0 : row0;
+    int lo = 0, hi = a.N;                          // largest s in [0, N) with cu[s] <= tf
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if ((int64_t)a.cu[mid] <= tf) lo = mid; else hi = mid;
+    }
+    return TileSeq{lo, a.cu[lo], a.cu[lo + 1], a.pool != nullptr ? a.slot_idx[lo] : -1};
+}
+
+// Row r of a tile of `rows` rows from token row0: position in its sequence (-1
+// outside every sequence), length, sequence, slot (-1 without a pool or out of
+// range).  Arithmetic when the first row's sequence covers the tile, else a
+// per-row search.
+__device__ __forceinline__ void tile_row(const FusedArgs& a, const TileSeq& f, int64_t row0, int rows, int r,
+                                         int& pos, int& len, int& seq, int& sid) {
+    const int64_t tf = row0 < 0 ? 0 : row0;
+    const int64_t t = row0 + r;
+    pos = -1; len = 0; seq = f.lo;
+    if (f.c0 <= tf && f.c1 >= row0 + rows) {
+        if (t >= tf) { pos = (int)(t - f.c0); len = (int)(f.c1 - f.c0); }
+    } else if (t >= 0 && t < a.total_T) {
+        int l2 = 0, h2 = a.N;
+        while (h2 - l2 > 1) {
+            const int mid = (l2 + h2) >> 1;
+            if ((int64_t)a.cu[mid] <= t) l2 = mid; else h2 = mid;
+        }
+        seq = l2;
+        const int64_t s0 = a.cu[l2], s1 = a.cu[l2 + 1];
+        if (t >= s0 && t < s1) { pos = (int)(t - s0); len = (int)(s1 - s0); }
+    }
+    sid = -1;
+    if (a.pool != nullptr && pos >= 0) {
+        const int64_t v = seq == f.lo ? f.slot_lo : a.slot_idx[seq];
+        sid = slot_ok(v, a.num_slots) ? (int)v : -1;
+    }
+}
+
 // Split tiles (fused_split.hip), for D in {1024, 1536, 2048}.
 // fused_split_choice: the split tiles' channel count (32 or 64) when their
 // expected span is shorter than `other`, the span of the other tile forms in

@@ -192,6 +192,13 @@ def fused_train_lfm2(seed: int = 6, T: int = 65536, H: int = H_LFM2, K: int = K_
     return fused_case(seed, [T], H, K, D)
 
 
+def fused_one_token_lfm2(seed: int = 8, N: int = 256, H: int = H_LFM2, K: int = K_LFM2,
+                         D: int = H_LFM2) -> FusedWorkload:
+    """N one-token sequences, each with its own slot (a decode-shaped batch through the fused prefill: every
+    conv history comes from the pool)."""
+    return fused_case(seed, [1] * N, H, K, D, slots=N + 16)
+
+
 def fused_ragged_lfm2(seed: int = 7, N: int = 8, lo: int = 64, hi: int = 2048, H: int = H_LFM2, K: int = K_LFM2,
                       D: int = H_LFM2) -> FusedWorkload:
     """Ragged prefill through the fused path: N sequences with lengths uniform on [lo, hi], one pool slot each."""
