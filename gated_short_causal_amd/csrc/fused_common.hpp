@@ -153,12 +153,15 @@ __device__ __forceinline__ void tile_row(const FusedArgs& a, const TileSeq& f, i
 }
 
 // Split tiles (fused_split.hip), for D in {1024, 1536, 2048}.
-// fused_split_choice: the split tiles' channel count (32 or 64) when their
-// expected span is shorter than `other`, the span of the other tile forms in
-// rounds of wide overlapping tiles; 0 otherwise.  LFM2SC_FUSED_SPLIT in the
-// environment overrides it: 0 never, 1 always, 32 or 64 always with that count.
+// fused_split_choice: 32 or 64 (split tiles of 64 rows and that many channels)
+// or 128 (mid tiles: 128 rows x 64 channels) when that form's expected span is
+// shorter than `other`, the span of the other tile forms in rounds of wide
+// overlapping tiles; 0 otherwise.  LFM2SC_FUSED_SPLIT in the environment
+// overrides it: 0 never, 1 always (the best of the three), 32, 64 or 128 always
+// that form.
 int fused_split_choice(int64_t total_T, int H, double other);
-// Sets the tile counts and launches the split-tile kernel (channel count nc).
+// Sets the tile counts and launches the split-tile (nc = 32, 64) or mid-tile
+// (nc = 128) kernel.
 hipError_t launch_fused_split(FusedArgs a, int K, int nc, hipStream_t s);
 
 }  // namespace lfm2sc

@@ -353,6 +353,256 @@ void fused_split_kernel(const FusedArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- mid tiles
+// Between the split tiles and the wide ones (T ~ 512 .. 1024 at H = 2048) a CU
+// has ~25k GEMM outputs to produce; the tile that stages the fewest bytes for
+// that is 128 rows x 64 channels (1.3 MB at D = 2048, one round at T = 1024,
+// against 2 rounds of 64-row split tiles or a 2.6 MB wide tile).  8 waves: k
+// half x row half x channel half, each wave 64 rows x 32 channels over its half
+// of D; the waves of a k half share its staged x and W_in rows, so the stages
+// meet at a workgroup barrier (3-slot ring, 2 stages in flight, as in the halo
+// form of the wide tile).  Halo rows, the two k halves' partial sums and the
+// LDS epilogue work as in the split tiles.
+constexpr int kMBM = 128;                      // token rows per mid tile (all of them outputs)
+constexpr int kMNC = 64;                       // channels per mid tile
+constexpr int kMThreads = 512;
+constexpr int kMHalf = 21 * 1024;              // one k half of a stage: x 8 KiB, halo block 1 KiB, W_in 12 KiB
+constexpr int kMHalo = 8 * 1024, kMW = 9 * 1024;
+constexpr int kMSlot = 48 * 1024;              // a ring slot (both k halves); after the reduction, 64 rows of partials
+constexpr int kMVm = 5;                        // loads per wave and stage (the halo block: one more for wave 0 of a half)
+constexpr int64_t mid_tiles(int64_t total_T, int H) { return (total_T + kMBM - 1) / kMBM * (H / kMNC); }
+
+// One wave's loads of a stage: blocks gi, gi+4 of the half's 8 x blocks, gi, gi+4,
+// gi+8 of its 12 W_in blocks, and for gi == 0 the halo block.
+__device__ __forceinline__ void mid_issue(rsrc_t xr, rsrc_t hr, rsrc_t wr, uint8_t* half, int gi,
+                                          const uint32_t* xoff, uint32_t hoff, const uint32_t* woff, uint32_t ko) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(half + (gi + 4 * i) * 1024), 16, xoff[i] + ko, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(half + kMW + (gi + 4 * i) * 1024), 16, woff[i] + ko, 0,
+                                                 0, 0);
+    if (gi == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(hr, (lds_ptr_t)(half + kMHalo), 16, hoff + ko, 0, 0, 0);
+}
+
+template <int K, int D>
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fused_mid_kernel(const FusedArgs a) {
+    using S = WideStage<32>;
+    using G = SplitGeom<kMNC>;                         // partial-sum layout of 64-row blocks
+    constexpr int NKH = D / 2 / 32;                    // stages (each covers 32 k of both halves)
+    static_assert(D % 64 == 0 && NKH >= 3, "whole stages, at least three");
+    constexpr int KH = K > 1 ? K - 1 : 1;
+    constexpr int kRpt = kMBM / (kMThreads / kMNC);    // epilogue rows per thread (16)
+    __shared__ __attribute__((aligned(16))) uint8_t r0[kMSlot], r1[kMSlot], r2[kMSlot];
+    __shared__ int s_pos[kMBM], s_len[kMBM], s_seq[kMBM], s_slot[kMBM];
+    __shared__ float s_hpart[KH][2 * kMNC];            // halo rows' B | xv (partials, then sums)
+
+    const int lin = xcd_tile(blockIdx.x, gridDim.x);
+    if (lin >= a.tiles_m * a.tiles_n) return;
+    int mt, nt;
+    fused_tile(lin, a.tiles_m, a.tiles_n, mt, nt);
+    const int tid = threadIdx.x;
+    const int wave = wave_id();
+    const int lane = tid & 63;
+    const int q = lane & 31, hl = lane >> 5;
+    const int kh = wave >> 2, rh = (wave >> 1) & 1, chh = wave & 1, gi = wave & 3;
+    const int H = a.H;
+    const int64_t T = a.total_T;
+    const int64_t row0 = (int64_t)mt * kMBM;
+    const int n0 = nt * kMNC;
+
+    {   // row map, before any load of the reduction
+        const TileSeq f = tile_first_seq(a, row0);
+        if (tid < kMBM) {
+            int pos, len, seq, sid;
+            tile_row(a, f, row0, kMBM, tid, pos, len, seq, sid);
+            s_pos[tid] = pos; s_len[tid] = len; s_seq[tid] = seq; s_slot[tid] = sid;
+        }
+    }
+
+    // ---------------------------------------------------------------- reduction
+    const int64_t vhi = (row0 + kMBM < T) ? row0 + kMBM : T;
+    const uint32_t xbytes = __builtin_amdgcn_readfirstlane((uint32_t)((vhi - row0) * a.x_stride * 2));
+    const rsrc_t xr = row_rsrc(a.x + row0 * a.x_stride, xbytes);
+    const int64_t hlo = row0 - (K - 1) < 0 ? 0 : row0 - (K - 1);
+    const uint32_t hbytes = __builtin_amdgcn_readfirstlane((uint32_t)((row0 - hlo) * a.x_stride * 2));
+    const rsrc_t hr = row_rsrc(a.x + hlo * a.x_stride, hbytes);
+    const rsrc_t wr = row_rsrc(a.W, (uint32_t)((int64_t)3 * H * D * 2));
+    const int brow = lane >> 2;
+    const uint32_t kq = (uint32_t)kh * D;              // byte offset of the half's k range (D/2 bf16)
+    uint32_t xoff[2], woff[3];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 16 * (gi + 4 * i) + brow;
+        int64_t t = row0 + r;
+        t = t >= vhi ? vhi - 1 : t;
+        xoff[i] = (uint32_t)((t - row0) * a.x_stride * 2) + kq + S::dma_chunk(lane, r);
+    }
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        const int n = 16 * (gi + 4 * i) + brow;
+        woff[i] = (uint32_t)(((int64_t)(n / kMNC) * H + n0 + (n % kMNC)) * D * 2) + kq + S::dma_chunk(lane, n);
+    }
+    uint32_t hoff;
+    {
+        const int64_t t = row0 - (K - 1) + brow;
+        hoff = (brow < K - 1 && t >= hlo) ? (uint32_t)((t - hlo) * a.x_stride * 2) + kq + S::dma_chunk(lane, brow)
+                                          : 0x80000000u;
+    }
+    auto half = [&](int u) -> uint8_t* { return (u == 0 ? r0 : u == 1 ? r1 : r2) + kh * kMHalf; };
+
+    f32x16 acc[2][3], acch[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) acc[i][j][r] = 0.f;
+        acch[0][r] = acch[1][r] = 0.f;
+    }
+
+    mid_issue(xr, hr, wr, half(0), gi, xoff, hoff, woff, 0);
+    mid_issue(xr, hr, wr, half(1), gi, xoff, hoff, woff, 64);
+    auto stage = [&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        constexpr int later = s + 1 < NKH ? 1 : 0;     // stages after s in flight
+        __builtin_amdgcn_sched_barrier(0);
+        if (gi == 0) wait_vm<later * (kMVm + 1)>(); else wait_vm<later * kMVm>();
+        stage_barrier();
+        if constexpr (s + 2 < NKH) mid_issue(xr, hr, wr, half((s + 2) % 3), gi, xoff, hoff, woff, (uint32_t)(s + 2) * 64);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t* h = half(s % 3);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int c = kk * 2 + hl;
+            bf16x8 fa[2], fb[3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(h + S::chunk(rh * 64 + i * 32 + q, c));
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8*>(h + kMW + S::chunk(j * kMNC + chh * 32 + q, c));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 3; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            if (K > 1 && rh == 0) {                    // halo rows: B and xv of this wave's channels
+                const bf16x8 fh = *reinterpret_cast<const bf16x8*>(h + kMHalo + S::chunk(q & 15, c));
+                acch[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, fb[0], acch[0], 0, 0, 0);
+                acch[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, fb[2], acch[1], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    unroll_stages<0, NKH>(stage);
+
+    // ---------------------------------------------------------------- epilogue
+    // Row half rh's partials [64][192] live in slot rh (after the ring drains):
+    // the k half 1 waves store theirs, the k half 0 waves add their own in place
+    // (each element read and written by the same lane), then every thread runs
+    // the conv for one channel and 16 consecutive rows.
+    lds_barrier();
+    float* const prt = reinterpret_cast<float*>(rh == 0 ? r0 : r1);
+    if (kh == 1) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    prt[G::pidx(i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3), j * kMNC + chh * 32 + q)] = acc[i][j][r];
+        if (rh == 0 && hl == 0) {
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) {
+                s_hpart[e][chh * 32 + q] = acch[0][e];
+                s_hpart[e][kMNC + chh * 32 + q] = acch[1][e];
+            }
+        }
+    }
+    lds_barrier();
+    if (kh == 0) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float* p = prt + G::pidx(i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3), j * kMNC + chh * 32 + q);
+                    *p = acc[i][j][r] + *p;
+                }
+        if (rh == 0 && hl == 0) {
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) {
+                s_hpart[e][chh * 32 + q] = acch[0][e] + s_hpart[e][chh * 32 + q];
+                s_hpart[e][kMNC + chh * 32 + q] = acch[1][e] + s_hpart[e][kMNC + chh * 32 + q];
+            }
+        }
+    }
+    lds_barrier();
+
+    const float* const p0 = reinterpret_cast<const float*>(r0);
+    const float* const p1 = reinterpret_cast<const float*>(r1);
+    auto psum = [&](int row, int col) { return (row < 64 ? p0 : p1)[G::pidx(row & 63, col)]; };
+    const int c = tid % kMNC;
+    const int grp = tid / kMNC;                        // rows kRpt*grp .. +kRpt
+    const int ch = n0 + c;
+    float wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
+    const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
+    float sv[kRpt][KH];
+#pragma unroll
+    for (int i = 0; i < kRpt; ++i) {
+        const int R = kRpt * grp + i;
+        const int pos = s_pos[R], slot = s_slot[R];
+#pragma unroll
+        for (int k = 0; k < KH; ++k) {
+            const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
+            const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
+                                       : a.w + (int64_t)ch * K;
+            sv[i][k] = need ? bf16_val(*src) : 0.f;
+        }
+    }
+    float hb[KH + kRpt];                               // bx of rows kRpt*grp - (K-1) .. kRpt*grp + kRpt - 1
+#pragma unroll
+    for (int m = 0; m < K - 1; ++m) {
+        const int rr = kRpt * grp - (K - 1) + m;
+        hb[m] = rr >= 0 ? psum(rr, c) * psum(rr, 2 * kMNC + c) : s_hpart[m][c] * s_hpart[m][kMNC + c];
+    }
+#pragma unroll
+    for (int i = 0; i < kRpt; ++i) hb[K - 1 + i] = psum(kRpt * grp + i, c) * psum(kRpt * grp + i, 2 * kMNC + c);
+#pragma unroll
+    for (int i = 0; i < kRpt; ++i) {
+        const int R = kRpt * grp + i;
+        const int pos = s_pos[R];
+        if (pos < 0) continue;
+        const float bxr = hb[K - 1 + i];
+        float h[KH];
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) h[k] = pos < K - 1 - k ? sv[i][k] : hb[i + k];
+        float conv = fmaf(wk[K - 1], bxr, bv);
+#pragma unroll
+        for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], h[k], conv);
+        const int64_t t = row0 + R;
+        const float cg = psum(R, kMNC + c);
+        a.y[t * a.y_stride + ch] = bf16_bits(cg * conv);
+        if (a.io != nullptr) {
+            uint16_t* io = a.io + t * a.io_stride + ch;
+            io[0] = bf16_bits(psum(R, c));
+            io[H] = bf16_bits(cg);
+            io[2 * H] = bf16_bits(psum(R, 2 * kMNC + c));
+        }
+        if (a.fin != nullptr && pos == s_len[R] - 1) {
+            uint16_t* f = a.fin + (int64_t)s_seq[R] * H * K + (int64_t)ch * K;
+#pragma unroll
+            for (int e = 0; e < K - 1; ++e) f[e] = bf16_bits(h[e]);
+            f[K - 1] = bf16_bits(bxr);
+        }
+    }
+}
+
 template <int K, int D, int NC>
 static void split_launch(const FusedArgs& a, int blocks, hipStream_t s) {
     hipLaunchKernelGGL((fused_split_kernel<K, D, NC>), dim3(blocks), dim3(kSThreads), 0, s, a);
@@ -367,7 +617,29 @@ static void split_k(const FusedArgs& a, int blocks, hipStream_t s) {
     }
 }
 
+template <int K>
+static void mid_k(const FusedArgs& a, int blocks, hipStream_t s) {
+    switch (a.D) {
+        case 1024: hipLaunchKernelGGL((fused_mid_kernel<K, 1024>), dim3(blocks), dim3(kMThreads), 0, s, a); break;
+        case 1536: hipLaunchKernelGGL((fused_mid_kernel<K, 1536>), dim3(blocks), dim3(kMThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((fused_mid_kernel<K, 2048>), dim3(blocks), dim3(kMThreads), 0, s, a); break;
+    }
+}
+
 hipError_t launch_fused_split(FusedArgs a, int K, int nc, hipStream_t s) {
+    if (nc == kMBM) {                                  // mid tiles: 128 rows x 64 channels
+        a.tiles_n = a.H / kMNC;
+        a.tiles_m = (int)((a.total_T + kMBM - 1) / kMBM);
+        const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
+        switch (K) {
+            case 1: mid_k<1>(a, blocks, s); break;
+            case 2: mid_k<2>(a, blocks, s); break;
+            case 3: mid_k<3>(a, blocks, s); break;
+            case 4: mid_k<4>(a, blocks, s); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     a.tiles_n = a.H / nc;
     a.tiles_m = (int)((a.total_T + kSBM - 1) / kSBM);
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
@@ -385,20 +657,23 @@ hipError_t launch_fused_split(FusedArgs a, int K, int nc, hipStream_t s) {
     return hipGetLastError();
 }
 
-// A split tile's cost relative to a wide overlapping tile, measured on MI355X at
-// D = H = 2048 (it follows the bytes a tile stages: 1.1 MB at 64 channels, 0.7
-// MB at 32, 2.6 MB for the wide tile).
-constexpr double kSplitTileCost64 = 0.45, kSplitTileCost32 = 0.30;
+// A split or mid tile's cost relative to a wide overlapping tile, measured on
+// MI355X at D = H = 2048 (it follows the bytes a tile stages: 1.1 MB for a split
+// tile of 64 channels, 0.7 MB at 32, 1.3 MB for a mid tile, 2.6 MB for the wide
+// tile).
+constexpr double kSplitTileCost64 = 0.45, kSplitTileCost32 = 0.30, kMidTileCost = 0.60;
 
 int fused_split_choice(int64_t total_T, int H, double other) {
     const bool ok64 = H % 64 == 0 && split_tiles(total_T, H, 64) < (1 << 30);
     const bool ok32 = H % 32 == 0 && split_tiles(total_T, H, 32) < (1 << 30);
+    const bool okm = H % kMNC == 0 && mid_tiles(total_T, H) < (1 << 30);
     bool force = false;
     if (const char* e = getenv("LFM2SC_FUSED_SPLIT")) {
         const std::string v(e);
         if (v == "0") return 0;
         if (v == "64") return ok64 ? 64 : 0;
         if (v == "32") return ok32 ? 32 : 0;
+        if (v == "128") return okm ? kMBM : 0;
         force = v == "1";
     }
     static const int resident = [] {
@@ -415,10 +690,13 @@ int fused_split_choice(int64_t total_T, int H, double other) {
     auto span = [&](int64_t tiles, double cost) { return (double)((tiles + resident - 1) / resident) * cost; };
     const double s64 = ok64 ? span(split_tiles(total_T, H, 64), kSplitTileCost64) : 1e300;
     const double s32 = ok32 ? span(split_tiles(total_T, H, 32), kSplitTileCost32) : 1e300;
-    if (!ok64 && !ok32) return 0;
-    const int best = s32 < s64 ? 32 : 64;
+    const double sm = okm ? span(mid_tiles(total_T, H), kMidTileCost) : 1e300;
+    if (!ok64 && !ok32 && !okm) return 0;
+    int best = s32 < s64 ? 32 : 64;
+    double bs = std::min(s32, s64);
+    if (sm < bs) { best = kMBM; bs = sm; }
     if (force) return best;
-    return std::min(s32, s64) < other ? best : 0;
+    return bs < other ? best : 0;
 }
 
 }  // namespace lfm2sc

@@ -261,11 +261,11 @@ const char* lfm2sc_last_error(void);
  * a GEMM into bf16 in_proj and then lfm2sc_prefill_ragged.  For D in {1024,
  * 1536, 2048} the call picks a tiling by size: wide tiles (H % 128 == 0) with
  * or without halo rows, or, for short inputs, split tiles whose waves each sum
- * a quarter of D (the fp32 sums, and so the results, may differ by rounding
- * between tilings; each is deterministic).  For testing, the environment
- * variables LFM2SC_FUSED_SPLIT (0: never split tiles, 1: always, 32 or 64:
- * always, with that many channels per tile) and LFM2SC_FUSED_HALO (0 or 1)
- * force one.
+ * a quarter of D, or mid tiles whose waves each sum half of it (the fp32 sums,
+ * and so the results, may differ by rounding between tilings; each is
+ * deterministic).  For testing, the environment variables LFM2SC_FUSED_SPLIT
+ * (0: never split or mid tiles, 1: always, 32 or 64: split tiles with that
+ * many channels, 128: mid tiles) and LFM2SC_FUSED_HALO (0 or 1) force one.
  */
 int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
                          const void* x, int64_t x_stride, int64_t total_T,

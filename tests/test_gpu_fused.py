@@ -18,12 +18,14 @@ DEV = "cuda"
 BF = torch.bfloat16
 
 # For D in {1024, 1536, 2048} the library picks a tile form per call by expected span: wide tiles (H % 128 == 0)
-# overlapping by K-1 rows, wide tiles with K-1 halo rows, or split tiles (64 rows x 32 or 64 channels, each of
-# the 4 waves reducing a quarter of D, K-1 halo rows).  LFM2SC_FUSED_SPLIT and LFM2SC_FUSED_HALO force one.
+# overlapping by K-1 rows, wide tiles with K-1 halo rows, split tiles (64 rows x 32 or 64 channels, each of the
+# 4 waves reducing a quarter of D, K-1 halo rows) or mid tiles (128 rows x 64 channels, 8 waves, two halves of
+# D, K-1 halo rows).  LFM2SC_FUSED_SPLIT and LFM2SC_FUSED_HALO force one.
 FORMS = {"overlap": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "0"},
          "halo": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "1"},
          "split32": {"LFM2SC_FUSED_SPLIT": "32"},
-         "split64": {"LFM2SC_FUSED_SPLIT": "64"}}
+         "split64": {"LFM2SC_FUSED_SPLIT": "64"},
+         "mid": {"LFM2SC_FUSED_SPLIT": "128"}}
 
 
 @pytest.fixture(params=sorted(FORMS))
@@ -119,6 +121,29 @@ def test_fused_out_of_range_slots():
     assert_close(y[4:], y_ref_zero[4:], BF, "rows of out-of-range slots")
     assert_close(pool[1], p_ok[1], BF, "valid slot state")
     for s in (0, 2, 3, 4):
+        assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
+
+
+@pytest.mark.parametrize("nc", ["32", "64", "128"])
+def test_fused_split_out_of_range_slots(nc, monkeypatch):
+    """Split tiles with slot ids outside the pool: those sequences start from a zero state and write no state;
+    a valid slot still gets its final state; the other slots stay untouched."""
+    monkeypatch.setenv("LFM2SC_FUSED_SPLIT", nc)
+    lens = [4, 70, 2, 1]
+    _say(f"case: fused split{nc} out-of-range slot ids H=128 D=1024")
+    c = wl.fused_case(516, lens, H=128, K=3, D=1024, slots=6)
+    c.slot_idx = torch.tensor([1, 6, -2, 4], dtype=torch.int32)
+    y, io, pool = _run(c)
+    zero = c.pool.clone()
+    zero[:] = 0
+    y_ok, p_ok, _ = oracle.fused_prefill(c.x, c.W_in, c.cu, c.w, c.pool, torch.tensor([1, 2, 3, 4]))
+    y_zero, _, _ = oracle.fused_prefill(c.x, c.W_in, c.cu, c.w, zero, torch.tensor([0, 1, 2, 3]))
+    assert_close(y[:4], y_ok[:4], BF, "valid slot rows")
+    assert_close(y[4:76], y_zero[4:76], BF, "rows of out-of-range slots")
+    assert_close(y[76:], y_ok[76:], BF, "valid slot rows after them")
+    assert_close(pool[1], p_ok[1], BF, "valid slot state")
+    assert_close(pool[4], p_ok[4], BF, "valid slot state")
+    for s in (0, 2, 3, 5):
         assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
 
 
@@ -242,15 +267,15 @@ def test_fused_wide_tile_boundaries(K, form):
     _check(c, y, io, pool, f"boundaries K={K}")
 
 
-@pytest.mark.parametrize("nc", ["32", "64"])
+@pytest.mark.parametrize("nc", ["32", "64", "128"])
 @pytest.mark.parametrize("K", [1, 2, 3, 4])
 @pytest.mark.parametrize("H", [64, 192])
 def test_fused_split_tiles(K, H, nc, monkeypatch):
-    """Split tiles of 32 and 64 channels also serve channel counts that are not multiples of 128.  A split tile
-    starts at a multiple of 64 rows and takes the history of its first K-1 rows from halo rows: sequences that
-    end exactly at such a boundary, one row before and one row after it, a 2-token sequence across it, sequences
-    shorter than K, an empty one, a sequence over several tiles, rows after the last sequence, padded rows, a
-    pool, a bias."""
+    """Split tiles of 32 and 64 channels and mid tiles (nc = 128: 128 rows x 64 channels) also serve channel
+    counts that are not multiples of 128.  A split tile starts at a multiple of 64 rows (a mid tile at a
+    multiple of 128) and takes the history of its first K-1 rows from halo rows: sequences that end exactly at
+    such a boundary, one row before and one row after it, a 2-token sequence across it, sequences shorter than
+    K, an empty one, a sequence over several tiles, rows after the last sequence, padded rows, a pool, a bias."""
     monkeypatch.setenv("LFM2SC_FUSED_SPLIT", nc)
     lens = [64, 63, 2, 65, 1, 0, 190, 5, 1, 2]
     _say(f"case: fused split tiles nc={nc} K={K} H={H} D=1024 lens={lens} padded, tail rows")

@@ -72,11 +72,12 @@ def test_decode_pool_beyond_2g_elements():
     assert_bits(pool[sl.long()].cpu(), rounded(p_ref, BF), "states of the named slots")
 
 
-@pytest.mark.parametrize("form", ["overlap", "halo", "split32", "split64"])
+@pytest.mark.parametrize("form", ["overlap", "halo", "split32", "split64", "mid"])
 def test_fused_forward_300k_tokens(form, monkeypatch):
-    """Every tile form (wide tiles overlapping or with halo rows, split tiles of 32 or 64 channels) at ~300k
-    tokens: tile and row offsets in 64 bits."""
-    monkeypatch.setenv("LFM2SC_FUSED_SPLIT", form[5:] if form.startswith("split") else "0")
+    """Every tile form (wide tiles overlapping or with halo rows, split tiles of 32 or 64 channels, mid tiles)
+    at ~300k tokens: tile and row offsets in 64 bits."""
+    split = {"split32": "32", "split64": "64", "mid": "128"}.get(form, "0")
+    monkeypatch.setenv("LFM2SC_FUSED_SPLIT", split)
     monkeypatch.setenv("LFM2SC_FUSED_HALO", "1" if form == "halo" else "0")
     lens = [300_000, 4097, 1]
     _say(f"case: fused forward lens={lens} D=H=2048 form={form}, sampled channels")
