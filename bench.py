@@ -309,8 +309,8 @@ def shape_measurements(wl_mod, steps):
 def fused_measurements(wl_mod, steps):
     """The fused in_proj + ShortConv forward (lfm2sc_fused_prefill) at the LFM2-1.2B layer shape (D = H = 2048):
     the training forward at T=65536 (y only, and with the in_proj output the backward takes), the ragged
-    prefill, short forwards (T=4096: one round of halo tiles; T=256 and 256 one-token sequences with a pool:
-    split tiles).  Matrix-core bound: FLOPs = 2 * T * D * 3H
+    prefill, short forwards (T=4096: one round of halo tiles; T=1024: mid tiles; T=256 and 256 one-token
+    sequences with a pool: split tiles).  Matrix-core bound: FLOPs = 2 * T * D * 3H
     per call against the bf16 dense peak.  `unfused_ms` is the two-step path it replaces, a bf16 GEMM into
     in_proj (torch.matmul) then lfm2sc_prefill_ragged: context, not a lower bound."""
     import torch
@@ -333,8 +333,10 @@ def fused_measurements(wl_mod, steps):
         gemm = lambda: torch.matmul(g.x, g.W_in.t(), out=ip)
         conv = lambda: lfm2sc_prefill_ragged(ip, g.cu, g.w, y, g.pool, g.slot_idx)
         if graph:
-            ms = graph_time([fused], steps)
-            unf = graph_time([gemm], steps) + graph_time([conv], steps)
+            # 8 back-to-back calls per graph (per pair of calls for the two-step path), so that the gap
+            # between graph replays is spread over them as it is over the calls of a serving loop
+            ms = graph_time([fused] * 8, steps)
+            unf = 2 * graph_time([gemm, conv] * 8, steps)
         else:
             # the inputs were just generated on the host with the GPU idle: warm up long enough for the
             # long calls to reach their steady rate (the same for both paths)
@@ -352,6 +354,7 @@ def fused_measurements(wl_mod, steps):
     one("fused_train_T65536_with_in_proj", wl_mod.fused_train_lfm2(T=65536), True, False)
     one("fused_ragged_prefill_N8", wl_mod.fused_ragged_lfm2(), False, True)
     one("fused_train_T4096", wl_mod.fused_train_lfm2(T=4096), False, True)
+    one("fused_short_T1024", wl_mod.fused_train_lfm2(T=1024), False, True)
     one("fused_short_T256", wl_mod.fused_train_lfm2(T=256), False, True)
     one("fused_one_token_N256", wl_mod.fused_one_token_lfm2(), False, True)
     return out
