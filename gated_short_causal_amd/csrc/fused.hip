@@ -100,6 +100,26 @@ struct RowMap {
     const int* slot;
 };
 
+// Does the quad R0..R0+3 need the general epilogue below?  Only when one of
+// its output rows is among a sequence's first K-1 (its history starts from
+// the initial state, not from the rows before it) or ends a sequence whose
+// final state is wanted; every other quad of a multi-sequence tile takes the
+// plain conv over the rows before it, the same code as a one-sequence tile.
+template <int K>
+__device__ __forceinline__ bool quad_special(const FusedArgs& a, const RowMap& rm, int R0, int first_out) {
+    const int4 p4 = *reinterpret_cast<const int4*>(rm.pos + R0);
+    const int4 l4 = *reinterpret_cast<const int4*>(rm.len + R0);
+    const int pos[4] = {p4.x, p4.y, p4.z, p4.w};
+    const int len[4] = {l4.x, l4.y, l4.z, l4.w};
+    bool sp = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const bool out = R0 + j >= first_out && pos[j] >= 0;
+        sp = sp || (out && (pos[j] < K - 1 || (a.fin != nullptr && pos[j] == len[j] - 1)));
+    }
+    return sp;
+}
+
 // The general (multi-sequence) epilogue for the 4 consecutive rows R0..R0+3
 // that one lane holds in an accumulator quad (rows before first_out are the
 // tile's history rows, not outputs).  hx holds bx of rows R0-(K-1) ..
@@ -115,26 +135,38 @@ __device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& r
                                              const float (&wk)[K], float bv, const float* hx, const float* cgate,
                                              Out&& out) {
     constexpr int KH = K > 1 ? K - 1 : 1;
+    // the quad's positions and lengths in two 16-byte LDS reads (read row by
+    // row, each length check waited on the LDS before the next row)
     const int4 p4 = *reinterpret_cast<const int4*>(rm.pos + R0);
+    const int4 l4 = *reinterpret_cast<const int4*>(rm.len + R0);
     const int pos[4] = {p4.x, p4.y, p4.z, p4.w};
+    const int len[4] = {l4.x, l4.y, l4.z, l4.w};
     float sv[4][KH];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int k = 0; k < KH; ++k) sv[j][k] = 0.f;
     if (a.pool != nullptr) {
         const int4 s4 = *reinterpret_cast<const int4*>(rm.slot + R0);
         const int slot[4] = {s4.x, s4.y, s4.z, s4.w};
+        // Only a sequence's first K-1 rows take state entries: a quad without
+        // one skips the fetch (a wave none of whose lanes has one branches
+        // around it), so the other quads do not wait on loads.
+        bool any = false;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) any = any || (pos[j] >= 0 && pos[j] < K - 1 && R0 + j >= first_out && slot[j] >= 0);
+        if (any) {
 #pragma unroll
-            for (int k = 0; k < K - 1; ++k) {
-                const bool need = pos[j] >= 0 && pos[j] < K - 1 - k && R0 + j >= first_out && slot[j] >= 0;
-                const uint16_t* src = need ? a.pool + (int64_t)slot[j] * a.slot_stride + (int64_t)ch * K + pos[j] + 1 + k
-                                           : a.w + (int64_t)ch * K;
-                sv[j][k] = need ? bf16_val(*src) : 0.f;
-            }
-    } else {
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int k = 0; k < KH; ++k) sv[j][k] = 0.f;
+                for (int k = 0; k < K - 1; ++k) {
+                    const bool need = pos[j] >= 0 && pos[j] < K - 1 - k && R0 + j >= first_out && slot[j] >= 0;
+                    const uint16_t* src = need ? a.pool + (int64_t)slot[j] * a.slot_stride + (int64_t)ch * K + pos[j] +
+                                                     1 + k
+                                               : a.w + (int64_t)ch * K;
+                    sv[j][k] = need ? bf16_val(*src) : 0.f;
+                }
+        }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -146,7 +178,7 @@ __device__ __forceinline__ void quad_general(const FusedArgs& a, const RowMap& r
         for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], h[k], conv);
         out(j, cgate[j] * conv);
         const int row = R0 + j;
-        if (a.fin != nullptr && row >= first_out && pos[j] >= 0 && pos[j] == rm.len[row] - 1) {
+        if (a.fin != nullptr && row >= first_out && pos[j] >= 0 && pos[j] == len[j] - 1) {
             uint16_t* f = a.fin + (int64_t)rm.seq[row] * a.H * K + (int64_t)ch * K;
 #pragma unroll
             for (int e = 0; e < K - 1; ++e) f[e] = bf16_bits(h[e]);
@@ -165,7 +197,8 @@ void fused_prefill_kernel(const FusedArgs a) {
         wring3[kFStageB];
     __shared__ __attribute__((aligned(16))) uint16_t ost[kFBM * kFOutStride];
     __shared__ __attribute__((aligned(16))) int s_pos[kFBM];
-    __shared__ int s_len[kFBM], s_seq[kFBM];
+    __shared__ __attribute__((aligned(16))) int s_len[kFBM];
+    __shared__ int s_seq[kFBM];
     __shared__ __attribute__((aligned(16))) int s_slot[kFBM];
     __shared__ float s_edge[2][32][4];        // bx of rows 125..127 of each channel (the second half's history)
 
@@ -398,13 +431,14 @@ void fused_prefill_kernel(const FusedArgs a) {
     // when final states are wanted): no per-row sequence logic.
     const int p0 = s_pos[0], pl = s_pos[kFBM - 1];
     const bool simple = p0 >= 0 && pl == p0 + kFBM - 1 && !(a.fin != nullptr && pl == s_len[kFBM - 1] - 1);
-    if (simple) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float hx[K - 1 + 4];
-                history(i, g, hx);
+        for (int g = 0; g < 4; ++g) {
+            const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
+            float hx[K - 1 + 4];
+            history(i, g, hx);
+            if (simple || !quad_special<K>(a, rm, R0, K - 1)) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
@@ -412,21 +446,13 @@ void fused_prefill_kernel(const FusedArgs a) {
                     for (int k = 0; k < K - 1; ++k) conv = fmaf(wk[k], hx[j + k], conv);
                     stage_out(i, 4 * g + j, acc[i][1][4 * g + j] * conv);
                 }
-            }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int R0 = wm * 128 + i * 32 + 8 * g + 4 * hl;
-                float hx[K - 1 + 4];
-                history(i, g, hx);
+            } else {
                 float cg[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cg[j] = acc[i][1][4 * g + j];
                 quad_general<K>(a, rm, R0, K - 1, ch, wk, bv, hx, cg, [&](int j, float v) { stage_out(i, 4 * g + j, v); });
             }
-    }
+        }
     flush_rows(a.y, a.y_stride, true);
 }
 
@@ -739,7 +765,7 @@ __device__ __forceinline__ void wide_tile(const FusedArgs& a, const WideLds& L) 
 #pragma unroll
             for (int m = 0; m < K - 1; ++m) prev[m] = tl[m];
             const int R0 = rbase + i * 32 + 8 * g + 4 * hl;
-            if (simple) {
+            if (simple || !quad_special<K>(a, rm, R0, kFirstOut)) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     float conv = fmaf(wk[K - 1], hx[K - 1 + j], bv);
@@ -872,7 +898,8 @@ static bool fused_use_halo(int64_t total_T, int tiles_n) {
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
     const bool unrolled = a.D == 1024 || a.D == 1536 || a.D == 2048;
-    const bool wide = a.H % kWNC == 0 && unrolled;
+    bool wide = a.H % kWNC == 0 && unrolled;
+    if (const char* e = getenv("LFM2SC_FUSED_WIDE")) wide = wide && e[0] != '0';   // 0: the 4-wave tile
     a.tiles_n = a.H / (wide ? kWNC : kFNC);
     const bool halo = wide && fused_use_halo<K>(a.total_T, a.tiles_n);
     const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows

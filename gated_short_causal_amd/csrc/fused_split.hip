@@ -290,16 +290,26 @@ void fused_split_kernel(const FusedArgs a) {
         // addresses chosen without branching (an entry not needed reads the
         // channel's weight instead).
         float sv[RPT][KH];
+        bool any = false;                              // does a row of this thread start a sequence?
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-            const int R = 32 * p + RPT * grp + i;
-            const int pos = s_pos[R], slot = s_slot[R];
+            const int pos = s_pos[32 * p + RPT * grp + i];
+            any = any || (pos >= 0 && pos < K - 1 && s_slot[32 * p + RPT * grp + i] >= 0);
 #pragma unroll
-            for (int k = 0; k < KH; ++k) {
-                const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
-                const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
-                                           : a.w + (int64_t)ch * K;
-                sv[i][k] = need ? bf16_val(*src) : 0.f;
+            for (int k = 0; k < KH; ++k) sv[i][k] = 0.f;
+        }
+        if (any) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int R = 32 * p + RPT * grp + i;
+                const int pos = s_pos[R], slot = s_slot[R];
+#pragma unroll
+                for (int k = 0; k < KH; ++k) {
+                    const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
+                    const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
+                                               : a.w + (int64_t)ch * K;
+                    sv[i][k] = need ? bf16_val(*src) : 0.f;
+                }
             }
         }
         // hb[m]: bx of row RPT*grp - (K-1) + m of this row tile
@@ -553,16 +563,26 @@ void fused_mid_kernel(const FusedArgs a) {
     for (int k = 0; k < K; ++k) wk[k] = bf16_val(a.w[(int64_t)ch * K + k]);
     const float bv = a.bias != nullptr ? bf16_val(a.bias[ch]) : 0.f;
     float sv[kRpt][KH];
+    bool any = false;                                  // does a row of this thread start a sequence?
 #pragma unroll
     for (int i = 0; i < kRpt; ++i) {
-        const int R = kRpt * grp + i;
-        const int pos = s_pos[R], slot = s_slot[R];
+        const int pos = s_pos[kRpt * grp + i];
+        any = any || (pos >= 0 && pos < K - 1 && s_slot[kRpt * grp + i] >= 0);
 #pragma unroll
-        for (int k = 0; k < KH; ++k) {
-            const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
-            const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
-                                       : a.w + (int64_t)ch * K;
-            sv[i][k] = need ? bf16_val(*src) : 0.f;
+        for (int k = 0; k < KH; ++k) sv[i][k] = 0.f;
+    }
+    if (any) {
+#pragma unroll
+        for (int i = 0; i < kRpt; ++i) {
+            const int R = kRpt * grp + i;
+            const int pos = s_pos[R], slot = s_slot[R];
+#pragma unroll
+            for (int k = 0; k < KH; ++k) {
+                const bool need = k < K - 1 && pos >= 0 && pos < K - 1 - k && slot >= 0;
+                const uint16_t* src = need ? a.pool + (int64_t)slot * a.slot_stride + (int64_t)ch * K + pos + 1 + k
+                                           : a.w + (int64_t)ch * K;
+                sv[i][k] = need ? bf16_val(*src) : 0.f;
+            }
         }
     }
     float hb[KH + kRpt];                               // bx of rows kRpt*grp - (K-1) .. kRpt*grp + kRpt - 1
