@@ -20,6 +20,8 @@
 // work at K = 3).  When H % 128 == 0 and D is one of the LFM2 hidden sizes a
 // wide variant (fused_wide_kernel) covers 128 channels with 8 waves instead,
 // the same 128 x 32 block per wave, which halves the x rows fetched per FLOP.
+// Short inputs, which fill too few of these tiles, take the split and mid
+// tiles of fused_split.hip; fused_k below picks the form per call.
 //
 // Reduction.  Stages of kFBK = 32 along D.  The x rows and W_in rows of a stage
 // go from global memory straight into one slot of a 4-deep LDS ring (buffer
@@ -858,10 +860,11 @@ static void fused_launch_wide(const FusedArgs& a, int blocks, hipStream_t s) {
 // overlapping one (measured on MI355X, D=H=2048: 88-90 us against 73-74 us
 // per round at T=32768 and 65536).  T up to 16384 takes halo tiles (T=4096:
 // 1 round instead of 2, 0.098 against 0.137 ms), larger T overlapping ones.
-// LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form.
+// LFM2SC_FUSED_HALO=0 or 1 in the environment forces a form (and
+// LFM2SC_FUSED_WIDE=0 the 4-wave tile instead of the wide one).
 constexpr double kHaloTileCost = 1.21;
 // A 4-wave tile's cost relative to a wide overlapping tile (1.8 against 2.6 MB
-// staged per tile; used only against split tiles).
+// staged per tile; used only against split and mid tiles).
 constexpr double kMainTileCost = 0.80;
 // Wide tiles resident on the device at once.
 template <int K>
@@ -904,7 +907,7 @@ static hipError_t fused_k(FusedArgs a, hipStream_t s) {
     const bool halo = wide && fused_use_halo<K>(a.total_T, a.tiles_n);
     const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows
     a.tiles_m = (int)((a.total_T + out - 1) / out);
-    if (unrolled) {   // split tiles when their expected span is shorter (short inputs)
+    if (unrolled) {   // split or mid tiles when their expected span is shorter (short inputs)
         const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, res = wide_resident<K>();
         const double other = (double)((tiles + res - 1) / res) * (wide ? (halo ? kHaloTileCost : 1.0) : kMainTileCost);
         const int nc = fused_split_choice(a.total_T, a.H, other);

@@ -265,7 +265,8 @@ const char* lfm2sc_last_error(void);
  * and so the results, may differ by rounding between tilings; each is
  * deterministic).  For testing, the environment variables LFM2SC_FUSED_SPLIT
  * (0: never split or mid tiles, 1: always, 32 or 64: split tiles with that
- * many channels, 128: mid tiles) and LFM2SC_FUSED_HALO (0 or 1) force one.
+ * many channels, 128: mid tiles), LFM2SC_FUSED_HALO (0 or 1) and
+ * LFM2SC_FUSED_WIDE (0: the 4-wave tile instead of the wide one) force one.
  */
 int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
                          const void* x, int64_t x_stride, int64_t total_T,

@@ -20,16 +20,20 @@ BF = torch.bfloat16
 # For D in {1024, 1536, 2048} the library picks a tile form per call by expected span: wide tiles (H % 128 == 0)
 # overlapping by K-1 rows, wide tiles with K-1 halo rows, split tiles (64 rows x 32 or 64 channels, each of the
 # 4 waves reducing a quarter of D, K-1 halo rows) or mid tiles (128 rows x 64 channels, 8 waves, two halves of
-# D, K-1 halo rows).  LFM2SC_FUSED_SPLIT and LFM2SC_FUSED_HALO force one.
+# D, K-1 halo rows); the 4-wave tile (256 rows x 64 channels, "narrow") serves the other shapes.
+# LFM2SC_FUSED_SPLIT, LFM2SC_FUSED_HALO and LFM2SC_FUSED_WIDE force one.
 FORMS = {"overlap": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "0"},
          "halo": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_HALO": "1"},
          "split32": {"LFM2SC_FUSED_SPLIT": "32"},
          "split64": {"LFM2SC_FUSED_SPLIT": "64"},
-         "mid": {"LFM2SC_FUSED_SPLIT": "128"}}
+         "mid": {"LFM2SC_FUSED_SPLIT": "128"},
+         "narrow": {"LFM2SC_FUSED_SPLIT": "0", "LFM2SC_FUSED_WIDE": "0"}}
 
 
 @pytest.fixture(params=sorted(FORMS))
 def form(request, monkeypatch):
+    for k in ("LFM2SC_FUSED_SPLIT", "LFM2SC_FUSED_HALO", "LFM2SC_FUSED_WIDE"):
+        monkeypatch.delenv(k, raising=False)
     for k, v in FORMS[request.param].items():
         monkeypatch.setenv(k, v)
     return request.param
