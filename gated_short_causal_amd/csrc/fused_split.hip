@@ -696,6 +696,7 @@ int fused_split_choice(int64_t total_T, int H, double other) {
         if (v == "128") return okm ? kMBM : 0;
         force = v == "1";
     }
+    // workgroups resident at once: split and mid tiles both fit one per CU (LDS)
     static const int resident = [] {
         int dev = 0, cus = 0, per = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
