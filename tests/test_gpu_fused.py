@@ -304,3 +304,44 @@ def test_fused_one_token_sequences_lfm2_shape():
     assert_close(y[:, chans], y_ref, BF, "y (sampled)")
     assert_close(io[:, rows], ip_ref, BF, "in_proj_out (sampled)")
     assert_close(pool[:, chans, :], p_ref, BF, "final states (sampled)")
+
+
+@pytest.mark.parametrize("seed", [580, 581, 582])
+def test_fused_random_ragged_all_forms(seed, form):
+    """Seeded random ragged batches (1-40 sequences, lengths 0-300 with many short ones, a pool with out-of-range
+    slots mixed in, a bias, padded rows) through every tile form at H = 128, D = 1024, K drawn from 1-4."""
+    g = torch.Generator().manual_seed(seed)
+    N = int(torch.randint(1, 41, (1,), generator=g))
+    short = torch.randint(0, 4, (N,), generator=g)
+    long_ = torch.randint(0, 301, (N,), generator=g)
+    pick = torch.rand(N, generator=g) < 0.4
+    lens = torch.where(pick, short, long_).tolist()
+    K = int(torch.randint(1, 5, (1,), generator=g))
+    _say(f"case: fused random ragged seed={seed} N={N} K={K} T={sum(lens)} {form} tiles")
+    c = wl.fused_case(seed, lens, H=128, K=K, D=1024, slots=N + 3, bias=True, x_pad=8, tail_rows=3)
+    bad = torch.rand(N, generator=g) < 0.15
+    c.slot_idx = torch.where(bad, torch.full_like(c.slot_idx, -1), c.slot_idx)
+    y, io, pool = _run(c, with_io=True, y_pad=8)
+    zero_for_bad = c.pool.clone()
+    # the oracle's reading of an out-of-range slot: zero initial state, nothing written; give those sequences
+    # spare slots filled with zeros and compare the states of the valid slots only
+    spare = [s for s in range(N + 3) if s not in set(c.slot_idx.tolist())]
+    sl = c.slot_idx.clone()
+    for i in torch.nonzero(bad).flatten().tolist():
+        sl[i] = spare.pop()
+        zero_for_bad[sl[i]] = 0
+    y_ref, p_ref, ip_ref = oracle.fused_prefill(c.x[:, : c.D], c.W_in, c.cu, c.w, zero_for_bad, sl, bias=c.bias)
+    covered = int(c.cu[-1])
+    assert_close(y[:covered], y_ref[:covered], BF, "y")
+    assert_close(io[:covered], ip_ref[:covered], BF, "in_proj_out")
+    for i in range(N):
+        s = int(c.slot_idx[i])
+        if s >= 0:
+            if lens[i] > 0:
+                assert_close(pool[s], p_ref[s], BF, f"state of sequence {i}")
+            else:
+                assert_bits(pool[s], c.pool[s], f"slot of empty sequence {i} untouched")
+    named = {int(s) for s in c.slot_idx.tolist() if s >= 0}
+    for s in range(N + 3):
+        if s not in named:
+            assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
