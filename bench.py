@@ -360,6 +360,23 @@ def fused_measurements(wl_mod, steps):
     return out
 
 
+def fused_only(args):
+    """The fused in_proj + ShortConv training forward at D = H = 2048, T = args.T (y only): `warmup` untimed
+    calls, then `steps` timed ones; one JSON line with the time and the algorithmic bytes of a call (x rows
+    read, W_in read once, y written, the weight)."""
+    import torch
+    from gated_short_causal_amd import lfm2sc_fused_prefill
+    from gated_short_causal_amd import workloads as wl_mod
+    c = wl_mod.fused_train_lfm2(T=args.T).to(torch.device("cuda"))
+    T, H, D = c.x.shape[0], c.H, c.D
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    call = lambda: lfm2sc_fused_prefill(c.x, c.W_in, c.cu, c.w, y)
+    ms = timed_loop(call, args.steps, args.warmup)
+    algo = T * D * 2 + 3 * H * D * 2 + T * H * 2 + H * c.K * 2
+    print(json.dumps({"fused_only": {"T": T, "ms": round(ms, 5), "TFLOP/s": round(2.0 * T * D * 3 * H / ms / 1e9, 1),
+                                     "algorithmic_bytes_per_call": algo}}), flush=True)
+
+
 def calibrate_copy():
     """A plain device-to-device copy of 1 GiB, 5 times: the FETCH_SIZE / WRITE_SIZE readings of this kernel
     under rocprofv3 give the counter-to-bytes factor (1 GiB read and 1 GiB written per dispatch)."""
@@ -386,6 +403,8 @@ def main():
                     help="skip the decode, ragged prefill and verify figures (graph replay, a few seconds)")
     ap.add_argument("--extra", dest="extra", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--fused-only", action="store_true",
+                    help="only the fused in_proj + ShortConv training forward (y only), for counter passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the ShortConv path is sharded by channels or "
@@ -395,6 +414,9 @@ def main():
     import torch
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.fused_only:
+        fused_only(args)
         return
     from gated_short_causal_amd import lfm2sc_backward, lfm2sc_backward_workspace_bytes, lfm2sc_prefill_ragged
     from gated_short_causal_amd import workloads as wl
