@@ -460,8 +460,8 @@ void fused_prefill_kernel(const FusedArgs a) {
 
 // ---------------------------------------------------------------- wide tiles
 // The tile above fetches 28 KiB per 32-deep stage for its MFMA work; on
-// MI355X its loop waits on the vector-memory data path (L2 -> CU), which
-// hardware counters show busy ~80% of the time.  Wide tiles cover 128
+// MI355X its loop waits on those loads (they do not hide under the MFMA work,
+// though L2 could deliver them three times faster).  Wide tiles cover 128
 // channels with 8 waves (two per SIMD), each wave still 128 rows x 32
 // channels, so a stage moves 1.4x fewer bytes per FLOP.  Used when H % 128 ==
 // 0 and D is one of the unrolled hidden sizes.

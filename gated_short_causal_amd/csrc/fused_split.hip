@@ -14,9 +14,9 @@
 namespace lfm2sc {
 
 // ---------------------------------------------------------------- split tiles
-// A tile's time is set by the bytes it stages (x rows and W_in rows over all of
-// D), which reach one CU's LDS at a roughly fixed rate on MI355X: a wide tile
-// stages 2.6 MB at D = 2048 (~75 us).  Short inputs fill few tiles (T = 256:
+// A tile's time follows the bytes it stages (x rows and W_in rows over all of
+// D), which these loops draw at a roughly fixed rate per CU on MI355X (about a
+// third of what L2 delivers): a wide tile stages 2.6 MB at D = 2048 (~75 us).  Short inputs fill few tiles (T = 256:
 // 16 wide tiles for 256 CUs; any T up to 4096 one round or less), so their
 // time is that of one tile.  A split tile is 64 rows x NC channels (NC = 64:
 // 1.1 MB at D = 2048; NC = 32: 0.7 MB), and its 4 waves each reduce their own
