@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     lfm2sc_conv_update,
     lfm2sc_decode_step,
     lfm2sc_fused_prefill,
+    lfm2sc_fused_prefill_plan,
     lfm2sc_fused_prefill_workspace_bytes,
     lfm2sc_prefill_ragged,
     lfm2sc_verify_window,

@@ -167,6 +167,12 @@ def lfm2sc_fused_prefill_workspace_bytes(dtype, H, K, num_seqs, with_pool) -> in
     return int(_lib.lib().lfm2sc_fused_prefill_workspace_bytes(code, H, K, num_seqs, int(bool(with_pool))))
 
 
+def lfm2sc_fused_prefill_plan(H, K, D, total_T) -> int:
+    """The tiling lfm2sc_fused_prefill takes for these sizes: 1 wide tiles, 2 wide tiles with halo rows, 3 the
+    4-wave tile, 32 / 64 split tiles, 128 mid tiles, 0 for no token; negative for sizes it rejects."""
+    return int(_lib.lib().lfm2sc_fused_prefill_plan(H, K, D, total_T))
+
+
 def lfm2sc_fused_prefill(x, W_in, cu_seqlens, weight, y, state_pool=None, slot_idx=None, bias=None,
                          in_proj_out=None, workspace=None):
     """in_proj (x @ W_in^T, on the matrix cores) fused with the ShortConv prefill.  x [rows, >=D] bf16,

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "fused_common.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -418,6 +419,15 @@ size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seq
     if (dtype != LFM2SC_BF16 || H < 64 || H % 64 != 0 || H > kMaxH || K < 1 || K > 4 || num_seqs < 0) return 0;
     if (!with_pool) return 0;
     return ((size_t)num_seqs * (size_t)H * (size_t)K * 2 + 255) / 256 * 256;
+}
+
+int lfm2sc_fused_prefill_plan(int H, int K, int D, int64_t total_T) {
+    if (H < 64 || H % 64 != 0 || H > kMaxH || K < 1 || K > 4 || D < fused_depth_multiple() ||
+        D % fused_depth_multiple() != 0 || (int64_t)3 * H * D * 2 >= ((int64_t)1 << 31) || total_T < 0 ||
+        total_T >= kMaxRows)
+        return -LFM2SC_ERR_BAD_SHAPE;
+    if (total_T == 0) return 0;
+    return fused_plan(K, total_T, H, D);
 }
 
 int lfm2sc_fused_prefill(int dtype, int H, int K, int D, const void* x, int64_t x_stride, int64_t total_T,

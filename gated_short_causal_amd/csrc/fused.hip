@@ -898,24 +898,48 @@ static bool fused_use_halo(int64_t total_T, int tiles_n) {
 }
 
 
+// The tiling of a call: kPlanWide, kPlanWideHalo, kPlanMain (the 4-wave tile),
+// or a split / mid tile's channel-or-row code from fused_split_choice (32, 64,
+// 128).
+constexpr int kPlanWide = 1, kPlanWideHalo = 2, kPlanMain = 3;
+template <int K>
+static int fused_plan_k(int64_t total_T, int H, int D) {
+    const bool unrolled = D == 1024 || D == 1536 || D == 2048;
+    bool wide = H % kWNC == 0 && unrolled;
+    if (const char* e = getenv("LFM2SC_FUSED_WIDE")) wide = wide && e[0] != '0';   // 0: the 4-wave tile
+    const int tiles_n = H / (wide ? kWNC : kFNC);
+    const bool halo = wide && fused_use_halo<K>(total_T, tiles_n);
+    const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows
+    if (unrolled) {   // split or mid tiles when their expected span is shorter (short inputs)
+        const int64_t tiles = (total_T + out - 1) / out * tiles_n, res = wide_resident<K>();
+        const double other = (double)((tiles + res - 1) / res) * (wide ? (halo ? kHaloTileCost : 1.0) : kMainTileCost);
+        const int nc = fused_split_choice(total_T, H, other);
+        if (nc != 0) return nc;
+    }
+    return wide ? (halo ? kPlanWideHalo : kPlanWide) : kPlanMain;
+}
+
+int fused_plan(int K, int64_t total_T, int H, int D) {
+    switch (K) {
+        case 1: return fused_plan_k<1>(total_T, H, D);
+        case 2: return fused_plan_k<2>(total_T, H, D);
+        case 3: return fused_plan_k<3>(total_T, H, D);
+        case 4: return fused_plan_k<4>(total_T, H, D);
+    }
+    return -1;
+}
+
 template <int K>
 static hipError_t fused_k(FusedArgs a, hipStream_t s) {
-    const bool unrolled = a.D == 1024 || a.D == 1536 || a.D == 2048;
-    bool wide = a.H % kWNC == 0 && unrolled;
-    if (const char* e = getenv("LFM2SC_FUSED_WIDE")) wide = wide && e[0] != '0';   // 0: the 4-wave tile
-    a.tiles_n = a.H / (wide ? kWNC : kFNC);
-    const bool halo = wide && fused_use_halo<K>(a.total_T, a.tiles_n);
-    const int64_t out = halo ? kFBM : fused_out_rows<K>();     // halo tiles output all their rows
-    a.tiles_m = (int)((a.total_T + out - 1) / out);
-    if (unrolled) {   // split or mid tiles when their expected span is shorter (short inputs)
-        const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n, res = wide_resident<K>();
-        const double other = (double)((tiles + res - 1) / res) * (wide ? (halo ? kHaloTileCost : 1.0) : kMainTileCost);
-        const int nc = fused_split_choice(a.total_T, a.H, other);
-        if (nc != 0) {
-            const hipError_t e = launch_fused_split(a, K, nc, s);
-            return e != hipSuccess ? e : fused_commit(a, K, s);
-        }
+    const int plan = fused_plan_k<K>(a.total_T, a.H, a.D);
+    if (plan != kPlanWide && plan != kPlanWideHalo && plan != kPlanMain) {
+        const hipError_t e = launch_fused_split(a, K, plan, s);
+        return e != hipSuccess ? e : fused_commit(a, K, s);
     }
+    const bool wide = plan != kPlanMain, halo = plan == kPlanWideHalo;
+    a.tiles_n = a.H / (wide ? kWNC : kFNC);
+    const int64_t out = halo ? kFBM : fused_out_rows<K>();
+    a.tiles_m = (int)((a.total_T + out - 1) / out);
     const int blocks = pad_xcd(a.tiles_m * a.tiles_n);
     if (wide) {
         auto go = [&](auto halo_c) {

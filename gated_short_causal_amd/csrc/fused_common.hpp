@@ -163,5 +163,8 @@ int fused_split_choice(int64_t total_T, int H, double other);
 // Sets the tile counts and launches the split-tile (nc = 32, 64) or mid-tile
 // (nc = 128) kernel.
 hipError_t launch_fused_split(FusedArgs a, int K, int nc, hipStream_t s);
+// The tiling lfm2sc_fused_prefill takes (fused.hip): 1 wide tiles, 2 wide tiles
+// with halo rows, 3 the 4-wave tile, 32 / 64 split tiles, 128 mid tiles.
+int fused_plan(int K, int64_t total_T, int H, int D);
 
 }  // namespace lfm2sc

@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define LFM2SC_ABI_VERSION 4
+#define LFM2SC_ABI_VERSION 5
 
 enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
 
@@ -279,6 +279,19 @@ int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
 
 /* Workspace bytes of lfm2sc_fused_prefill (0 when with_pool is 0). */
 size_t lfm2sc_fused_prefill_workspace_bytes(int dtype, int H, int K, int num_seqs, int with_pool);
+
+/*
+ * The tiling lfm2sc_fused_prefill takes for these sizes, for tests and tuning
+ * (host only: the one device query, the number of resident workgroups, falls
+ * back to 256 without a device).  1: wide tiles (256 rows x 128 channels),
+ * 2: wide tiles with halo rows, 3: the 4-wave tile (256 rows x 64 channels),
+ * 32 or 64: split tiles of 64 rows and that many channels, 128: mid tiles
+ * (128 rows x 64 channels); 0 when total_T == 0 (nothing is launched).  The
+ * environment overrides named at lfm2sc_fused_prefill apply.  Returns
+ * -LFM2SC_ERR_BAD_SHAPE for sizes lfm2sc_fused_prefill rejects (H, K, D as
+ * there; total_T outside [0, 2^31)).
+ */
+int lfm2sc_fused_prefill_plan(int H, int K, int D, int64_t total_T);
 
 /*
  * Conv update of gated inputs in [batch][channel][token] order with arbitrary

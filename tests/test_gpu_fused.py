@@ -345,3 +345,14 @@ def test_fused_random_ragged_all_forms(seed, form):
     for s in range(N + 3):
         if s not in named:
             assert_bits(pool[s], c.pool[s], f"slot {s} untouched")
+
+
+def test_fused_plan_on_the_device(monkeypatch):
+    """On MI355X the occupancy query behind the tiling choice gives one workgroup per CU for each tile form, so
+    the plans match the ones worked out for 256 resident workgroups (tests/test_fused_plan.py)."""
+    from gated_short_causal_amd import lfm2sc_fused_prefill_plan as plan
+    for k in ("LFM2SC_FUSED_SPLIT", "LFM2SC_FUSED_HALO", "LFM2SC_FUSED_WIDE"):
+        monkeypatch.delenv(k, raising=False)
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    expected = {64: 32, 256: 32, 512: 64, 768: 128, 1024: 128, 1536: 1, 2048: 1, 4096: 2, 8192: 2, 65536: 1}
+    assert {T: plan(2048, 3, 2048, T) for T in expected} == expected
