@@ -314,10 +314,12 @@ def fused_measurements(wl_mod, steps):
     per call against the bf16 dense peak.  `unfused_ms` is the two-step path it replaces, a bf16 GEMM into
     in_proj (torch.matmul) then lfm2sc_prefill_ragged: context, not a lower bound."""
     import torch
-    from gated_short_causal_amd import (lfm2sc_fused_prefill, lfm2sc_fused_prefill_workspace_bytes,
-                                        lfm2sc_prefill_ragged)
+    from gated_short_causal_amd import (lfm2sc_fused_prefill, lfm2sc_fused_prefill_plan,
+                                        lfm2sc_fused_prefill_workspace_bytes, lfm2sc_prefill_ragged)
     dev = torch.device("cuda")
     out = {}
+    tilings = {1: "wide", 2: "wide, halo rows", 3: "4-wave", 32: "split, 32 channels", 64: "split, 64 channels",
+               128: "mid"}
 
     def one(name, c, with_io, graph):
         g = c.to(dev)
@@ -348,7 +350,8 @@ def fused_measurements(wl_mod, steps):
         out[name] = {"ms": round(ms, 5), "TFLOP/s": round(tf, 1),
                      "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)},
-                     "unfused_ms": round(unf, 5), "T": T, "flops": flops}
+                     "unfused_ms": round(unf, 5), "T": T, "flops": flops,
+                     "tiling": tilings.get(lfm2sc_fused_prefill_plan(H, c.K, D, T), "?")}
 
     one("fused_train_T65536", wl_mod.fused_train_lfm2(T=65536), False, False)
     one("fused_train_T65536_with_in_proj", wl_mod.fused_train_lfm2(T=65536), True, False)
