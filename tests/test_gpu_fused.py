@@ -356,3 +356,20 @@ def test_fused_plan_on_the_device(monkeypatch):
     assert torch.cuda.get_device_properties(0).multi_processor_count == 256
     expected = {64: 32, 256: 32, 512: 64, 768: 128, 1024: 128, 1536: 1, 2048: 1, 4096: 2, 8192: 2, 65536: 1}
     assert {T: plan(2048, 3, 2048, T) for T in expected} == expected
+
+
+def test_fused_wider_channels_sampled(form):
+    """H = 4096 channels (twice LFM2-1.2B's) at D = 2048 over ragged sequences with a pool, every tile form;
+    the oracle computes sampled channels, including the last tile's."""
+    lens = [900, 3, 1200, 1]
+    _say(f"case: fused H=4096 D=2048 lens={lens} pool, sampled channels, {form} tiles")
+    c = wl.fused_case(590, lens, H=4096, K=3, D=2048, slots=6, bias=True)
+    y, io, pool = _run(c, with_io=True)
+    chans = torch.tensor([0, 31, 32, 127, 128, 2047, 2048, 3000, 4031, 4032, 4095])
+    H = c.H
+    rows = torch.cat([chans, chans + H, chans + 2 * H])
+    y_ref, p_ref, ip_ref = oracle.fused_prefill(c.x, c.W_in[rows], c.cu, c.w[chans], c.pool[:, chans, :],
+                                                c.slot_idx, bias=c.bias[chans])
+    assert_close(y[:, chans], y_ref, BF, "y (sampled)")
+    assert_close(io[:, rows], ip_ref, BF, "in_proj_out (sampled)")
+    assert_close(pool[:, chans, :], p_ref, BF, "final states (sampled)")
