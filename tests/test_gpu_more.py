@@ -239,20 +239,29 @@ res.append(status(lambda: lfm2sc_prefill_ragged(c.inp, badcu, c.w, y, c.pool, c.
 win = torch.zeros(4, 2, 512, 3, dtype=torch.bfloat16, device=dev)
 acc = torch.tensor([0, 1, 3, 2], dtype=torch.int32, device=dev)
 res.append(status(lambda: lfm2sc_commit_window(win, acc, c.pool, c.slot_idx)))
+from gated_short_causal_amd import lfm2sc_fused_prefill, lfm2sc_fused_prefill_workspace_bytes
+f = wl.fused_case(81, [3, 5, 2, 6], H=512, K=3, D=1024, slots=8).to(dev)
+yf = torch.empty(16, 512, dtype=torch.bfloat16, device=dev)
+ws = torch.empty(lfm2sc_fused_prefill_workspace_bytes(torch.bfloat16, 512, 3, 4, True), dtype=torch.uint8, device=dev)
+res.append(status(lambda: lfm2sc_fused_prefill(f.x, f.W_in, f.cu, f.w, yf, f.pool, f.slot_idx, workspace=ws)))
+res.append(status(lambda: lfm2sc_fused_prefill(f.x, f.W_in, f.cu, f.w, yf, f.pool, dup, workspace=ws)))
+badcu16 = torch.tensor([0, 3, 2, 10, 16], dtype=torch.int32, device=dev)
+res.append(status(lambda: lfm2sc_fused_prefill(f.x, f.W_in, badcu16, f.w, yf, f.pool, f.slot_idx, workspace=ws)))
 print("STATUS", res, flush=True)
 """
 
 
 def test_check_mode_reports_bad_device_data():
     """With LFM2SC_CHECK=1 (read once per process, hence a child process) bad slot ids, row offsets and
-    accept lengths are reported as LFM2SC_ERR_PRECONDITION (6) and nothing is launched for them."""
+    accept lengths are reported as LFM2SC_ERR_PRECONDITION (6) and nothing is launched for them: decode, ragged
+    prefill, commit and the fused forward (valid inputs first, then duplicate slot ids, then bad row offsets)."""
     _say("case: LFM2SC_CHECK=1 in a child process")
     env = dict(os.environ, LFM2SC_CHECK="1")
     r = subprocess.run([sys.executable, "-c", _CHECK_SCRIPT, ROOT], env=env, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 0, r.stderr[-2000:]
     line = [l for l in r.stdout.splitlines() if l.startswith("STATUS")][0]
-    assert line == "STATUS [0, 6, 6, 6, 6]", line
+    assert line == "STATUS [0, 6, 6, 6, 6, 0, 6, 6]", line
 
 
 # ------------------------------------------------------------------ conv bias and state gradients (ABI v2)
