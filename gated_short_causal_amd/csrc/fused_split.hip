@@ -473,38 +473,60 @@ void fused_mid_kernel(const FusedArgs a) {
         acch[0][r] = acch[1][r] = 0.f;
     }
 
-    mid_issue(xr, hr, wr, half(0), gi, xoff, hoff, woff, 0);
-    mid_issue(xr, hr, wr, half(1), gi, xoff, hoff, woff, 64);
-    auto stage = [&](auto s_c) {
-        constexpr int s = decltype(s_c)::value;
-        constexpr int later = s + 1 < NKH ? 1 : 0;     // stages after s in flight
-        __builtin_amdgcn_sched_barrier(0);
-        if (gi == 0) wait_vm<later * (kMVm + 1)>(); else wait_vm<later * kMVm>();
-        stage_barrier();
-        if constexpr (s + 2 < NKH) mid_issue(xr, hr, wr, half((s + 2) % 3), gi, xoff, hoff, woff, (uint32_t)(s + 2) * 64);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint8_t* h = half(s % 3);
+    // Each stage's two k steps alternate between two fragment sets so that the
+    // LDS reads of one land under the MFMAs of the other: k step 1 of stage s is
+    // read during k step 0; then (barrier: stage s+1 has landed and every wave
+    // is done with stage s's slot) the slot is refilled with stage s+3 and k
+    // step 0 of stage s+1 is read during k step 1.  Two stages stay in flight
+    // (the three slots: one read, two landing).
+    struct Frags { bf16x8 a[2], b[3], h; };
+    auto read = [&](Frags& f, const uint8_t* h, int kk) {
+        const int c = kk * 2 + hl;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int c = kk * 2 + hl;
-            bf16x8 fa[2], fb[3];
+        for (int i = 0; i < 2; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(h + S::chunk(rh * 64 + i * 32 + q, c));
 #pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(h + S::chunk(rh * 64 + i * 32 + q, c));
+        for (int j = 0; j < 3; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(h + kMW + S::chunk(j * kMNC + chh * 32 + q, c));
+        if (K > 1 && rh == 0) f.h = *reinterpret_cast<const bf16x8*>(h + kMHalo + S::chunk(q & 15, c));
+    };
+    auto mma = [&](const Frags& f) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8*>(h + kMW + S::chunk(j * kMNC + chh * 32 + q, c));
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 3; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-            if (K > 1 && rh == 0) {                    // halo rows: B and xv of this wave's channels
-                const bf16x8 fh = *reinterpret_cast<const bf16x8*>(h + kMHalo + S::chunk(q & 15, c));
-                acch[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, fb[0], acch[0], 0, 0, 0);
-                acch[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, fb[2], acch[1], 0, 0, 0);
-            }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        if (K > 1 && rh == 0) {                        // halo rows: B and xv of this wave's channels
+            acch[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.h, f.b[0], acch[0], 0, 0, 0);
+            acch[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.h, f.b[2], acch[1], 0, 0, 0);
+        }
+    };
+    Frags f0, f1;
+    mid_issue(xr, hr, wr, half(0), gi, xoff, hoff, woff, 0);
+    mid_issue(xr, hr, wr, half(1), gi, xoff, hoff, woff, 64);
+    mid_issue(xr, hr, wr, half(2), gi, xoff, hoff, woff, 2 * 64);
+    if (gi == 0) wait_vm<2 * (kMVm + 1)>(); else wait_vm<2 * kMVm>();
+    stage_barrier();
+    read(f0, half(0), 0);
+    wait_lgkm0();
+    auto stage = [&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        read(f1, half(s % 3), 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkm0();
+        if constexpr (s + 1 < NKH) {
+            constexpr int later = s + 2 < NKH ? 1 : 0;     // stages after s+1 still in flight
+            if (gi == 0) wait_vm<later * (kMVm + 1)>(); else wait_vm<later * kMVm>();
+            stage_barrier();                               // stage s+1 landed; slot s % 3 read by every wave
+            if constexpr (s + 3 < NKH)
+                mid_issue(xr, hr, wr, half(s % 3), gi, xoff, hoff, woff, (uint32_t)(s + 3) * 64);
+            read(f0, half((s + 1) % 3), 0);
         }
         __builtin_amdgcn_sched_barrier(0);
+        mma(f1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s + 1 < NKH) wait_lgkm0();
     };
     unroll_stages<0, NKH>(stage);
 
