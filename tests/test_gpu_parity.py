@@ -176,22 +176,38 @@ def _channel_subset(c, chans):
     return sub, cols
 
 
-def test_train_T65536_sampled_channels():
-    _say("case: train bf16 T=65536 H=2048 K=3 (sampled channels + whole-output properties)")
-    c = wl.train_lfm2(T=65536)
+def _train_sampled(c, n_random, seed):
+    """The training step on the device at full size, then the oracle on the first and last 8 channels plus
+    `n_random` others (channels are independent, so the subset is exact for them)."""
+    H = c.H
     g = c.to(DEV)
     y = gpu_prefill(g)
     d_in, dW = gpu_backward(g)
     assert torch.isfinite(y).all() and torch.isfinite(d_in).all() and torch.isfinite(dW).all()
-    gen = torch.Generator().manual_seed(55)
-    chans = torch.cat([torch.arange(8), torch.arange(2040, 2048), torch.randperm(2032, generator=gen)[:112] + 8])
+    gen = torch.Generator().manual_seed(seed)
+    chans = torch.cat([torch.arange(8), torch.arange(H - 8, H), torch.randperm(H - 16, generator=gen)[:n_random] + 8])
     chans = torch.sort(chans).values
     sub, cols = _channel_subset(c, chans)
+    T = c.inp.shape[0]
     y_ref, _ = oracle.prefill(sub.inp, sub.cu, sub.w)
-    assert_close(y[:, chans.to(DEV)], y_ref, c.dtype, "T=65536 y (sampled channels)")
+    assert_close(y[:, chans.to(DEV)], y_ref, c.dtype, f"T={T} y (sampled channels)")
     d_ref, dW_ref = oracle.backward(sub.inp, sub.cu, sub.w, sub.dy)
-    assert_close(d_in[:, cols.to(DEV)], d_ref, c.dtype, "T=65536 d_in (sampled channels)")
-    assert_close(dW[chans.to(DEV)], dW_ref, c.dtype, "T=65536 dW (sampled channels)")
+    assert_close(d_in[:, cols.to(DEV)], d_ref, c.dtype, f"T={T} d_in (sampled channels)")
+    assert_close(dW[chans.to(DEV)], dW_ref, c.dtype, f"T={T} dW (sampled channels)")
+
+
+def test_train_T65536_sampled_channels():
+    _say("case: train bf16 T=65536 H=2048 K=3 (sampled channels + whole-output properties)")
+    _train_sampled(wl.train_lfm2(T=65536), 112, 55)
+
+
+@pytest.mark.parametrize("H,K,dtype", [(1024, 3, torch.bfloat16), (1536, 3, torch.bfloat16), (2048, 2, torch.bfloat16),
+                                       (2048, 4, torch.bfloat16), (2048, 3, torch.float32)])
+def test_train_T65536_other_shapes_sampled(H, K, dtype):
+    """The other channel counts, tap counts and I/O type that bench.py times at T=65536, in that launch
+    configuration (one 65,536-token sequence, zero state): sampled channels against the oracle."""
+    _say(f"case: train T=65536 H={H} K={K} {dtype} (sampled channels)")
+    _train_sampled(wl.train_lfm2(seed=60 + K, T=65536, H=H, K=K, dtype=dtype), 24, 56 + H + K)
 
 
 # ------------------------------------------------------------------ edge cases
