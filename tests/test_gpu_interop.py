@@ -61,6 +61,24 @@ def test_conv_update_with_tape(kind, K, L, dtype, H):
 
 
 @pytest.mark.parametrize("kind", ["sglang_view", "dense_nhl"])
+def test_conv_update_bench_shape(kind):
+    """The shape bench.py times (64 sequences x 8 tokens, H = 2048, K = 3, bf16, a tape, no bias, 64 of 256
+    slots), in both of its layouts: every output against the oracle, the tape bit for bit."""
+    N, L, H, K, dtype = 64, 8, 2048, 3, torch.bfloat16
+    _say(f"case: conv_update bench shape {kind} N={N} L={L} H={H} K={K}")
+    rows, w, _, pool, sl = _inputs(870, N, H, K, L, 256, dtype)
+    bx, out = _layout(rows, N, L, H, kind)
+    gpool = pool.to(DEV)
+    win = torch.full((N, L, H, K), float("nan"), dtype=dtype, device=DEV)
+    lfm2sc_conv_update(bx, w.to(DEV), gpool, sl.to(DEV), out, windows=win)
+    torch.cuda.synchronize()
+    out_ref, tape_ref, _ = oracle.conv_update(rows.view(N, L, H).transpose(1, 2), w, pool, sl)
+    assert_close(out, out_ref, dtype, "out")
+    assert_bits(win, rounded(tape_ref, dtype), "tape")
+    assert_bits(gpool, pool, "pool untouched with a tape")
+
+
+@pytest.mark.parametrize("kind", ["sglang_view", "dense_nhl"])
 @pytest.mark.parametrize("K,L,dtype", [(3, 1, torch.bfloat16), (3, 9, torch.bfloat16), (4, 3, torch.float32)])
 def test_conv_update_in_place(kind, K, L, dtype):
     N, H = 5, 1024

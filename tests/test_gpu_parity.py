@@ -101,6 +101,24 @@ def test_decode_lfm2_bf16():
     assert_bits(g.pool[mask.to(DEV)], pool0[mask.to(DEV)], "decode untouched slots")
 
 
+def test_decode_lfm2_bf16_N4096():
+    """The larger decode batch bench.py times: 4096 sequences of an 8192-slot pool, full compare."""
+    _say("case: decode bf16 N=4096 pool=8192 H=2048 K=3")
+    c = wl.decode_lfm2(seed=250, N=4096, slots=8192)
+    g = c.to(DEV)
+    pool0 = g.pool.clone()
+    y = _nan_like((4096, c.H), c.dtype)
+    lfm2sc_decode_step(g.inp, g.w, g.pool, g.slot_idx, y)
+    torch.cuda.synchronize()
+    y_ref, pool_ref = oracle.decode(c.inp, c.w, c.pool, c.slot_idx)
+    assert_close(y, y_ref, c.dtype, "decode y")
+    used = c.slot_idx.long()
+    assert_bits(g.pool[used.to(DEV)], rounded(pool_ref[used.numpy()], c.dtype), "decode written slots")
+    mask = torch.ones(8192, dtype=torch.bool)
+    mask[used] = False
+    assert_bits(g.pool[mask.to(DEV)], pool0[mask.to(DEV)], "decode untouched slots")
+
+
 # ------------------------------------------------------------------ ragged prefill
 
 def test_ragged_prefill_lfm2_bf16():
