@@ -463,14 +463,14 @@ void fused_mid_kernel(const FusedArgs a) {
     }
     auto half = [&](int u) -> uint8_t* { return (u == 0 ? r0 : u == 1 ? r1 : r2) + kh * kMHalf; };
 
-    f32x16 acc[2][3], acch[2];
+    f32x16 acc[2][3], acch;                            // acch: halo rows, B (row half 0) or xv (row half 1)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j) acc[i][j][r] = 0.f;
-        acch[0][r] = acch[1][r] = 0.f;
+        acch[r] = 0.f;
     }
 
     // Each stage's two k steps alternate between two fragment sets so that the
@@ -486,7 +486,7 @@ void fused_mid_kernel(const FusedArgs a) {
         for (int i = 0; i < 2; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(h + S::chunk(rh * 64 + i * 32 + q, c));
 #pragma unroll
         for (int j = 0; j < 3; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(h + kMW + S::chunk(j * kMNC + chh * 32 + q, c));
-        if (K > 1 && rh == 0) f.h = *reinterpret_cast<const bf16x8*>(h + kMHalo + S::chunk(q & 15, c));
+        if (K > 1) f.h = *reinterpret_cast<const bf16x8*>(h + kMHalo + S::chunk(q & 15, c));
     };
     auto mma = [&](const Frags& f) {
 #pragma unroll
@@ -494,10 +494,8 @@ void fused_mid_kernel(const FusedArgs a) {
 #pragma unroll
             for (int j = 0; j < 3; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-        if (K > 1 && rh == 0) {                        // halo rows: B and xv of this wave's channels
-            acch[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.h, f.b[0], acch[0], 0, 0, 0);
-            acch[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.h, f.b[2], acch[1], 0, 0, 0);
-        }
+        if (K > 1)                                     // halo rows: the row halves split B and xv, balancing the SIMDs
+            acch = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.h, rh == 0 ? f.b[0] : f.b[2], acch, 0, 0, 0);
     };
     Frags f0, f1;
     mid_issue(xr, hr, wr, half(0), gi, xoff, hoff, woff, 0);
@@ -545,12 +543,9 @@ void fused_mid_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     prt[G::pidx(i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3), j * kMNC + chh * 32 + q)] = acc[i][j][r];
-        if (rh == 0 && hl == 0) {
+        if (hl == 0) {
 #pragma unroll
-            for (int e = 0; e < K - 1; ++e) {
-                s_hpart[e][chh * 32 + q] = acch[0][e];
-                s_hpart[e][kMNC + chh * 32 + q] = acch[1][e];
-            }
+            for (int e = 0; e < K - 1; ++e) s_hpart[e][rh * kMNC + chh * 32 + q] = acch[e];
         }
     }
     lds_barrier();
@@ -564,12 +559,10 @@ void fused_mid_kernel(const FusedArgs a) {
                     float* p = prt + G::pidx(i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3), j * kMNC + chh * 32 + q);
                     *p = acc[i][j][r] + *p;
                 }
-        if (rh == 0 && hl == 0) {
+        if (hl == 0) {
 #pragma unroll
-            for (int e = 0; e < K - 1; ++e) {
-                s_hpart[e][chh * 32 + q] = acch[0][e] + s_hpart[e][chh * 32 + q];
-                s_hpart[e][kMNC + chh * 32 + q] = acch[1][e] + s_hpart[e][kMNC + chh * 32 + q];
-            }
+            for (int e = 0; e < K - 1; ++e)
+                s_hpart[e][rh * kMNC + chh * 32 + q] = acch[e] + s_hpart[e][rh * kMNC + chh * 32 + q];
         }
     }
     lds_barrier();
