@@ -371,8 +371,10 @@ void fused_split_kernel(const FusedArgs a) {
 // half x row half x channel half, each wave 64 rows x 32 channels over its half
 // of D; the waves of a k half share its staged x and W_in rows, so the stages
 // meet at a workgroup barrier (3-slot ring, 2 stages in flight, as in the halo
-// form of the wide tile).  Halo rows, the two k halves' partial sums and the
-// LDS epilogue work as in the split tiles.
+// form of the wide tile).  The halo rows' B and xv come from one more MFMA row
+// tile per k step, B in the row half 0 waves and xv in the row half 1 waves;
+// the two k halves' partial sums and the LDS epilogue work as in the split
+// tiles.
 constexpr int kMBM = 128;                      // token rows per mid tile (all of them outputs)
 constexpr int kMNC = 64;                       // channels per mid tile
 constexpr int kMThreads = 512;
