@@ -410,7 +410,7 @@ def main():
                     help="only the fused in_proj + ShortConv training forward (y only), for counter passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the ShortConv path is sharded by channels or "
+        print("bench.py measures one GPU only; the ShortConv path is sharded by channels or "
               "sequences with no collective on the hot path, and no multi-GPU figure is produced.", file=sys.stderr)
         sys.exit(2)
 
