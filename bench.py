@@ -96,11 +96,20 @@ def cpu_model():
     return "unknown"
 
 
+def host_cpus():
+    """CPUs this process may run on (the machine's CPU share for one GPU is 16; the oracle uses at most that)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(wl_mod, T, H, K, n_channels, min_seconds=10.0, single_channels=64):
     """The fp64 oracle (as it stands) on the same workload restricted to n_channels channels
     (channels are independent, so this is the same arithmetic on a slice).  Whole passes with
-    min(16, available) OpenMP threads until min_seconds have elapsed (value: median pass), then
-    three single-threaded passes over the first `single_channels` channels (median)."""
+    min(16, host CPUs) OpenMP threads (16 = one GPU's share of the host) until min_seconds have elapsed
+    (value: median pass), then three single-threaded passes over the first `single_channels` channels
+    (median); then every other workload (cpu_baseline_configs)."""
     import statistics
     import torch
     import oracle
@@ -117,7 +126,7 @@ def cpu_baseline(wl_mod, T, H, K, n_channels, min_seconds=10.0, single_channels=
         oracle.backward(inp, c.cu, w, dy)
         return time.perf_counter() - t
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = min(16, host_cpus())
     oracle.set_threads(threads)
     inp, w, dy = sample(n_channels)
     times, t0 = [], time.perf_counter()
@@ -137,10 +146,61 @@ def cpu_baseline(wl_mod, T, H, K, n_channels, min_seconds=10.0, single_channels=
             "sample": f"fwd+bwd, T={T}, first {n_channels} of {H} channels, K={K}, bf16 inputs widened to fp64; "
                       f"median of {len(times)} passes ({dt:.2f} s wall)",
             "seconds": round(dt, 3), "passes": len(times), "pass_s_median": round(med, 4),
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), "host_cpus": host_cpus(),
+            "configs": cpu_baseline_configs(wl_mod, threads),
             "single_thread": {"value": round(bytes1 / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                               "sample": f"first {single_channels} channels, median of 3 passes",
                               "pass_s_median": round(t1, 4)}}
+
+
+def cpu_baseline_configs(wl_mod, threads, min_seconds=0.5):
+    """The fp64 oracle (as it stands) on the other workloads, each at `threads` OpenMP threads and single
+    threaded: calls repeated until `min_seconds` have elapsed, median call time, GB/s at the same algorithmic
+    bytes as the GPU figures.  Config 1 (tiny fp32) is its 64-token forward + backward; config 2 one decode
+    step; config 3 one ragged prefill; config 4 one verify window; config 5 at T=4096 the forward + backward."""
+    import statistics
+    import oracle
+
+    def timed(fn):
+        ts, t0 = [], time.perf_counter()
+        while True:
+            t = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t)
+            if time.perf_counter() - t0 >= min_seconds and len(ts) >= 3:
+                return statistics.median(ts), len(ts)
+
+    c1 = wl_mod.tiny_fp32()
+    c2 = wl_mod.decode_lfm2()
+    c3 = wl_mod.ragged_prefill_lfm2()
+    c4 = wl_mod.verify_lfm2()
+    c5 = wl_mod.train_lfm2(T=4096)
+    T3 = c3.inp.shape[0]
+    cases = {
+        "cfg1_tiny_fp32_fwd_bwd": (lambda: (oracle.prefill(c1.inp, c1.cu, c1.w),
+                                            oracle.backward(c1.inp, c1.cu, c1.w, c1.dy)),
+                                   algo_bytes_fwd(64, 256, 3, 4) + algo_bytes_bwd(64, 256, 3, 4)),
+        "cfg2_decode_N256": (lambda: oracle.decode(c2.inp, c2.w, c2.pool, c2.slot_idx),
+                             algo_bytes_decode(256, 2048, 3, 2)),
+        "cfg3_ragged_prefill_N8": (lambda: oracle.prefill(c3.inp, c3.cu, c3.w, c3.pool, c3.slot_idx),
+                                   algo_bytes_prefill(T3, 8, 2048, 3, 2)),
+        "cfg4_verify_64x8": (lambda: oracle.verify(c4.inp, c4.w, c4.pool, c4.slot_idx, 8),
+                             algo_bytes_verify(64, 8, 2048, 3, 2)),
+        "cfg5_train_T4096": (lambda: (oracle.prefill(c5.inp, c5.cu, c5.w),
+                                      oracle.backward(c5.inp, c5.cu, c5.w, c5.dy)),
+                             algo_bytes_fwd(4096, 2048, 3, 2) + algo_bytes_bwd(4096, 2048, 3, 2)),
+    }
+    out = {}
+    for name, (fn, nbytes) in cases.items():
+        row = {}
+        for n in (threads, 1):
+            oracle.set_threads(n)
+            med, calls = timed(fn)
+            row["threads_%d" % n] = {"ms": round(1e3 * med, 4), "GB/s": round(nbytes / med / 1e9, 4), "calls": calls}
+        row["bytes"] = int(nbytes)
+        out[name] = row
+    oracle.set_threads(threads)
+    return out
 
 
 def copy_ceiling(reps=10):
@@ -271,9 +331,37 @@ def extra_measurements(wl_mod, steps):
                  for st, b, o, t in zip(sets, bxs, outs, tapes)]
         record(f"conv_update_64x8_{kind}", calls, algo_bytes_conv_update(64, 8, 2048, 3, 2))
         del sets, bxs, outs, tapes, calls
+    out.update(train_t4096_measurement(wl_mod, steps))
     out.update(fused_measurements(wl_mod, steps))
     out.update(shape_measurements(wl_mod, steps))
     return out
+
+
+def train_t4096_measurement(wl_mod, steps, nsets=5):
+    """The training step (prefill forward + backward) at T=4096, H=2048, K=3, bf16: `nsets` independent input
+    sets (~134 MB each with outputs, 670 MB per pass, past the 256 MB Infinity Cache) taken in turn, so each
+    step reads from HBM.  `ms` per step by graph replay (launch overhead removed), `eager_ms` back to back."""
+    import torch
+    from gated_short_causal_amd import lfm2sc_backward, lfm2sc_backward_workspace_bytes, lfm2sc_prefill_ragged
+    dev = torch.device("cuda")
+    T, H, K = 4096, 2048, 3
+    sets = [wl_mod.train_lfm2(seed=510 + i, T=T).to(dev) for i in range(nsets)]
+    ws = torch.empty(max(16, lfm2sc_backward_workspace_bytes(torch.bfloat16, H, K, T, 1)), dtype=torch.uint8,
+                     device=dev)
+    dW = torch.empty(H, K, dtype=torch.float32, device=dev)
+    calls = []
+    for c in sets:
+        y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        d_in = torch.empty(T, 3 * H, dtype=torch.bfloat16, device=dev)
+        calls.append(lambda c=c, y=y: lfm2sc_prefill_ragged(c.inp, c.cu, c.w, y))
+        calls.append(lambda c=c, d_in=d_in: lfm2sc_backward(c.inp, c.cu, c.w, c.dy, d_in, dW, ws))
+    eager = timed_loop(lambda: [f() for f in calls], steps, 2) / nsets
+    ms = 2 * graph_time(calls, steps)
+    nbytes = algo_bytes_fwd(T, H, K, 2) + algo_bytes_bwd(T, H, K, 2)
+    return {"train_T4096": {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
+                            "pct_of_hbm_peak": round(100 * nbytes / ms / 1e6 / HBM_PEAK_GBS, 1),
+                            "eager_ms": round(eager, 5), "bytes": int(nbytes), "input_sets": nsets,
+                            "pages_mi325x_liger_fwd_bwd_ms": 0.463}}
 
 
 def shape_measurements(wl_mod, steps):
@@ -444,23 +532,24 @@ def main():
         fwd()
         bwd()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed region: exactly `steps` steps back to back, events only at its two ends (an event recorded
+    # between two calls costs several microseconds of stream time of its own)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    for s in range(args.steps):
-        ev[s][0].record()
+    for _ in range(args.steps):
         fwd()
-        ev[s][1].record()
         bwd()
-        ev[s][2].record()
     stop.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(stop) / args.steps
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    bwd_ms = sum(b.elapsed_time(cc) for _, b, cc in ev) / args.steps
-    # the median protocol beside the timed loop: 50 more steps, each call bracketed by events
+    # average duration of one backward call (the dominant launch), from `steps` back-to-back calls on the
+    # stream the library launches on; and of one forward call the same way
+    bwd_ms = timed_loop(bwd, args.steps, 2)
+    fwd_ms = timed_loop(fwd, args.steps, 2)
+    # the median protocol beside the timed loop: 50 more steps, each call bracketed by events (so each call's
+    # figure includes the cost of its events)
     import statistics
     ev50 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
     for s in range(50):
@@ -472,7 +561,8 @@ def main():
     torch.cuda.synchronize()
     median50 = {"fwd_ms": round(statistics.median(a.elapsed_time(b) for a, b, _ in ev50), 5),
                 "bwd_ms": round(statistics.median(b.elapsed_time(cc) for _, b, cc in ev50), 5),
-                "step_ms": round(statistics.median(a.elapsed_time(cc) for a, _, cc in ev50), 5), "reps": 50}
+                "step_ms": round(statistics.median(a.elapsed_time(cc) for a, _, cc in ev50), 5), "reps": 50,
+                "note": "events around every call"}
     step_bytes = algo_bytes_fwd(T, H, K, e) + algo_bytes_bwd(T, H, K, e)
     bwd_bytes = algo_bytes_bwd(T, H, K, e)
     value = step_bytes / ms_step / 1e6
@@ -501,7 +591,8 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(bwd_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(bwd_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "lfm2sc_backward (backward_kernel + dw_finish_kernel, one call)",
+                     "kernel": "lfm2sc_backward (backward_kernel + dw_finish_kernel, one call; average of "
+                               "back-to-back calls)",
                      "algorithmic_bytes_per_launch": bwd_bytes},
         "median_of_50": median50,
         "context": {"pages_mi325x_liger_fwd_bwd_ms": {"T=4096": 0.463, "T=65536": 8.083}},

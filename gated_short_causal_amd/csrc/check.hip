@@ -4,7 +4,11 @@
 // size arguments describe, whatever the device-side index data holds; these
 // checks only turn bad index data into an error code instead of silently
 // skipped or wrong work.  They synchronise the stream, so they are for
-// debugging only.
+// debugging only.  The result travels through one device flag per process,
+// so a process-wide lock keeps each call's reset, checks and read-back
+// together: calls from several host threads take turns.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,6 +48,8 @@ __global__ void check_accept_kernel(const int32_t* __restrict__ acc, int N, int 
 
 int check_device_preconditions(hipStream_t s, const int32_t* slot_idx, int N, int64_t num_slots,
                                const int32_t* cu, int64_t total_T, const int32_t* accept, int L, hipError_t* err) {
+    static std::mutex mu;
+    std::lock_guard<std::mutex> lock(mu);
     *err = hipSuccess;
     const int tb = 256;
     hipLaunchKernelGGL(check_reset_kernel, dim3(1), dim3(64), 0, s);

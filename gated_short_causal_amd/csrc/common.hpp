@@ -249,11 +249,12 @@ inline int pad_xcd(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 // Packed sequences are laid on a virtual axis on which sequence i occupies
 // [cu[i] + i*gap, cu[i+1] + i*gap): consecutive sequences are separated by
 // `gap` empty positions, so any window of at most `gap` positions meets at
-// most one sequence.  Fixed-size windows of that axis are the work units; the
-// number of windows is bounded by ceil(total_T / gap) + N, known on the host
-// without reading cu_seqlens.  Row offsets are clamped to [0, total_T], so a
-// malformed cu_seqlens can produce wrong results but never an out-of-bounds
-// access.
+// most one sequence.  Fixed-size windows of that axis are the work units.  The
+// last sequence ends at most at total_T + (N-1)*gap, so ceil(total_T / gap) +
+// N - 1 windows of `gap` positions cover every sequence; that count is known
+// on the host without reading cu_seqlens.  Row offsets are clamped to
+// [0, total_T], so a malformed cu_seqlens can produce wrong results but never
+// an out-of-bounds access.
 struct SeqSpan {
     int seq;        // sequence index
     int64_t r0;     // first packed row of the sequence
@@ -305,17 +306,20 @@ struct WgLayout {
 // multiple of 8 and each XCD runs `groups` workgroups for each of its windows,
 // so a chip-wide count (e.g. 85 windows x 3 groups = 255 <= 256) can still put
 // 33 workgroups on an XCD of 32 CUs and push one into a second round.
+// The N-1 gaps between sequences take N-1 of the window slots (one sequence,
+// the training step, uses every slot: all CUs of the round get work).
 inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, int tw) {
     const int64_t g = groups > 0 ? groups : 1;
+    const int64_t gaps = N > 1 ? N - 1 : 0;
     const int64_t per_xcd = (int64_t)resident * LFM2SC_ROUNDS / kXcds / g;
     const int64_t slots = (per_xcd > 0 ? per_xcd : 1) * kXcds;
-    const int64_t free = slots - N;
+    const int64_t free = slots - gaps;
     const int64_t denom = (int64_t)tw * (free >= 1 ? free : (slots > 0 ? slots : 1));
     int64_t sub = (total_T + denom - 1) / denom;
     if (sub < LFM2SC_SUB_MIN) sub = LFM2SC_SUB_MIN;
     if (sub > (1 << 24)) sub = 1 << 24;
     const int64_t gap = sub * tw;
-    return Tiling{(int)sub, (total_T + gap - 1) / gap + N};
+    return Tiling{(int)sub, (total_T + gap - 1) / gap + gaps};
 }
 
 // Workgroups of `kernel` (kThreads wide, no dynamic LDS) resident on the

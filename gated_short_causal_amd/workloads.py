@@ -249,3 +249,39 @@ def large_fused_on(device, seed: int, lens, H: int = H_LFM2, K: int = K_LFM2, D:
         pool = _normal_on(g, (slots, H, K), dt, device)
         slot_idx = torch.randperm(slots, generator=g, device=device)[:N].to(torch.int32)
     return FusedWorkload("large_fused", H, K, D, x, W_in, w, cu.to(device), pool=pool, slot_idx=slot_idx)
+
+
+def _small_int(g, shape, dtype, levels):
+    """Integers drawn uniformly from {-levels, ..., -1, 1, ..., levels} (no zero), as `dtype`."""
+    mag = torch.randint(1, levels + 1, shape, generator=g)
+    sign = torch.randint(0, 2, shape, generator=g) * 2 - 1
+    return (mag * sign).to(torch.float32).to(dtype)
+
+
+def integer_case(seed: int, lens, H: int = H_LFM2, K: int = K_LFM2, dtype=torch.bfloat16, slots: int = 0,
+                 levels: int = 3, bias: bool = False, d_final: bool = False) -> Workload:
+    """Inputs, dy, weight, optional bias, pool and final-state gradient drawn as small nonzero integers
+    ({-3..-1, 1..3} by default).  Such values are exact in bf16, and with |values| <= 3 every product and every
+    sum the op forms stays an integer below 2^8 per output element (below 2^24 for dW over 65,536 tokens), so
+    the exact result is representable and any correct implementation must reproduce it bit for bit.  A dropped
+    or doubled token changes dW by a nonzero integer.  `extra` holds "bias" and "d_final" when asked for."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(list(lens), dtype=torch.int64)
+    N = lens.numel()
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    if N:
+        cu[1:] = torch.cumsum(lens, 0).to(torch.int32)
+    total = int(cu[-1])
+    inp = _small_int(g, (total, 3 * H), dtype, levels)
+    w = _small_int(g, (H, K), dtype, levels)
+    dy = _small_int(g, (total, H), dtype, levels)
+    pool = slot_idx = None
+    if slots:
+        pool = _small_int(g, (slots, H, K), dtype, levels)
+        slot_idx = torch.randperm(slots, generator=g)[:N].to(torch.int32)
+    extra = {"lens": lens.tolist()}
+    if bias:
+        extra["bias"] = _small_int(g, (H,), dtype, levels)
+    if d_final:
+        extra["d_final"] = _small_int(g, (N, H, K), dtype, levels)
+    return Workload("integer_case", dtype, H, K, inp, w, cu=cu, pool=pool, slot_idx=slot_idx, dy=dy, extra=extra)

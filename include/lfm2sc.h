@@ -50,7 +50,10 @@
  *    to [0, total_T]; an accept length outside [0, L] commits nothing.  Set the
  *    environment variable LFM2SC_CHECK=1 to have each call verify these
  *    preconditions on the device, synchronise, and return
- *    LFM2SC_ERR_PRECONDITION when one fails (slow; for debugging).
+ *    LFM2SC_ERR_PRECONDITION when one fails (slow; for debugging).  The check
+ *    reads its verdict back through one device flag of the library, so
+ *    checking calls from several host threads take turns on a process-wide
+ *    lock (they stay correct, and each one synchronises its own stream).
  *  - Outputs must not overlap inputs.  Nothing is accumulated into an output:
  *    y, tape, d_in and dW are overwritten.  Rows of y / d_in that belong to no
  *    sequence (outside [cu_seqlens[0], cu_seqlens[N])) are not written.
