@@ -433,36 +433,53 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
 }
 
 // dW[h][k] (and dbias[h]) = sum over windows of the partial rows, column
-// h*(K+1)+k (+K): 32 columns x 32 row groups per workgroup, then a fixed-order
-// sum of the 32 row groups; one rounding to fp32 at the store.
-constexpr int kFinCols = 32;
-constexpr int kFinRows = 32;
+// h*(K+1)+k (+K).  A workgroup takes 16 chunks of 16 bytes of columns (64 fp32
+// or 32 fp64 columns) and 16 row groups: each thread sums the rows rg, rg+16,
+// ... of its chunk in that order, then 16 partial sums per column meet in LDS
+// and are added in row-group order.  Fixed order, one rounding to fp32 at the
+// store.
+constexpr int kFinQ = 16;    // 16-byte column chunks per workgroup
+constexpr int kFinRG = 16;   // row groups per workgroup
+constexpr int kFinThreads = kFinQ * kFinRG;
 
 template <typename A>
-__global__ __launch_bounds__(kFinCols * kFinRows) void dw_finish_kernel(const A* __restrict__ partial, int64_t ntiles,
-                                                                       int64_t H, int K, float* __restrict__ dW,
-                                                                       float* __restrict__ dbias) {
+__global__ __launch_bounds__(kFinThreads) void dw_finish_kernel(const A* __restrict__ partial, int64_t ntiles,
+                                                                 int64_t H, int K, float* __restrict__ dW,
+                                                                 float* __restrict__ dbias) {
+    constexpr int V = 16 / (int)sizeof(A);   // columns per 16-byte chunk
+    constexpr int kCols = kFinQ * V;         // columns per workgroup
     const int PC = K + 1;
-    const int64_t cols = H * PC;
-    const int col = threadIdx.x % kFinCols;
-    const int rg = threadIdx.x / kFinCols;
-    const int64_t j = (int64_t)blockIdx.x * kFinCols + col;
-    A s = (A)0;
-    if (j < cols) {
-#pragma unroll 8
-        for (int64_t r = rg; r < ntiles; r += kFinRows) s += partial[r * cols + j];
-    }
-    __shared__ A red[kFinRows][kFinCols + 1];
-    red[rg][col] = s;
-    __syncthreads();
-    if (rg == 0 && j < cols) {
-        A t = (A)0;
+    const int64_t cols = H * PC;             // a multiple of 8 (H % 8 == 0): chunks never straddle its end
+    const int q = threadIdx.x % kFinQ;
+    const int rg = threadIdx.x / kFinQ;
+    const int64_t c0 = (int64_t)blockIdx.x * kCols + (int64_t)q * V;
+    A s[V];
 #pragma unroll
-        for (int q = 0; q < kFinRows; ++q) t += red[q][col];
-        const int64_t h = j / PC;
-        const int k = (int)(j % PC);
-        if (k < K) dW[h * K + k] = (float)t;
-        else if (dbias != nullptr) dbias[h] = (float)t;
+    for (int v = 0; v < V; ++v) s[v] = (A)0;
+    if (c0 < cols) {
+#pragma unroll 4
+        for (int64_t r = rg; r < ntiles; r += kFinRG) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(partial + r * cols + c0);
+            const A* e = reinterpret_cast<const A*>(&raw);
+#pragma unroll
+            for (int v = 0; v < V; ++v) s[v] += e[v];
+        }
+    }
+    __shared__ A red[kFinRG][kCols + 1];
+#pragma unroll
+    for (int v = 0; v < V; ++v) red[rg][q * V + v] = s[v];
+    __syncthreads();
+    if (threadIdx.x < kCols) {
+        const int64_t j = (int64_t)blockIdx.x * kCols + threadIdx.x;
+        if (j < cols) {
+            A t = (A)0;
+#pragma unroll
+            for (int g = 0; g < kFinRG; ++g) t += red[g][threadIdx.x];
+            const int64_t h = j / PC;
+            const int k = (int)(j % PC);
+            if (k < K) dW[h * K + k] = (float)t;
+            else if (dbias != nullptr) dbias[h] = (float)t;
+        }
     }
 }
 
@@ -496,7 +513,8 @@ template <typename E, int K>
 static Tiling backward_tiling(int64_t total_T, int N, int H) {
     constexpr auto kernel = backward_kernel<E, K, bwd_unroll<E, K>()>;
     static const int resident = resident_workgroups(kernel, bwd_dyn_lds<E, K>());
-    return ragged_tiling(total_T, N, WgLayout<LFM2SC_BWD_TW>::groups(H), resident, LFM2SC_BWD_TW);
+    return ragged_tiling(total_T, N, WgLayout<LFM2SC_BWD_TW>::groups(H), resident, LFM2SC_BWD_TW,
+                         (int64_t)H * (int64_t)sizeof(E), kWinSpanBwd);
 }
 
 template <typename E, int K>
@@ -516,9 +534,9 @@ static hipError_t backward_k(BackwardArgs<E> a, hipStream_t s) {
         a.ntiles = 0;
     }
     const int64_t cols = (int64_t)a.H * kPartCols<K>;
-    hipLaunchKernelGGL((dw_finish_kernel<A>), dim3((unsigned)((cols + kFinCols - 1) / kFinCols)),
-                       dim3(kFinCols * kFinRows), 0, s, (const A*)a.partial, (int64_t)a.ntiles, (int64_t)a.H, K, a.dW,
-                       a.dbias);
+    const int64_t fin_cols = (int64_t)kFinQ * (16 / (int64_t)sizeof(A));
+    hipLaunchKernelGGL((dw_finish_kernel<A>), dim3((unsigned)((cols + fin_cols - 1) / fin_cols)), dim3(kFinThreads), 0,
+                       s, (const A*)a.partial, (int64_t)a.ntiles, (int64_t)a.H, K, a.dW, a.dbias);
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && a.dinit != nullptr && a.N > 0) {
         const int64_t HK = (int64_t)a.H * K;

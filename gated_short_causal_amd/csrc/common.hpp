@@ -306,9 +306,91 @@ struct WgLayout {
 // multiple of 8 and each XCD runs `groups` workgroups for each of its windows,
 // so a chip-wide count (e.g. 85 windows x 3 groups = 255 <= 256) can still put
 // 33 workgroups on an XCD of 32 CUs and push one into a second round.
+// Window length and HBM conflicts.  All windows of a launch stream at once,
+// their rows a fixed `sub` apart, so the HBM channels and banks that serve
+// them at any moment follow from the spacing sub * row_bytes: at some
+// spacings many windows land on the same ones and the kernels slow down by up
+// to 25% (measured on MI355X with every base alignment of the buffers tried:
+// the effect follows the spacing, not the addresses).  kWinRate holds the
+// backward kernel's measured rate for bf16 rows of H = 2048 (4 KiB rows of
+// dy and y, 12 KiB of in_proj and d_in) at one full round of windows, for
+// window lengths kWinLo .. kWinHi-1: (TB/s - 4.0) * 100, median of three
+// sweeps.  For that row geometry a launch takes, among the window lengths from
+// the shortest that fits one round to 1/span above it, the one with the best
+// measured rate.  A longer window leaves some CUs idle: the backward, bound by
+// HBM, hardly notices (at 40 of 64 windows per channel group it still runs at
+// 95% of the full round's rate) and searches 1/8 above; the forward loses
+// ~0.6% per idle window and searches 1/64 above.  Other row geometries take
+// the shortest window.
+constexpr int kWinLo = 64;
+constexpr int kWinHi = 1024;
+constexpr unsigned char kWinRate[kWinHi - kWinLo] = {
+     82, 100,  93,  86,  99,  93,  92,  96, 101,  97,  93,  85,  93,  98, 104, 100, 103,  95, 108, 103,
+    114, 104,   0, 115, 116, 117, 109, 114, 108, 102, 106,  55,  95, 102, 108, 101,  82, 108, 103, 109,
+    109, 115,  74, 108,  85,  89,  41, 111, 116, 108, 111, 113, 109,  96,  94,  77, 109, 103, 109, 102,
+    115,  76,  96,  23,  87,  15, 108,  91, 110, 105, 103,  91, 119, 121, 100,  91, 115,  97, 113, 115,
+    114, 104, 114, 115,  97,  99,  90,  67, 111,  20, 118,  67, 126, 101, 128, 125, 119, 133, 111, 136,
+    135,  89,  99, 121, 135, 118, 113, 126,  66, 120, 123, 117, 120, 124, 133, 130, 134, 134, 137, 124,
+    128, 126, 124, 109, 123, 125,  66, 110, 102,  12, 109, 117, 113,   0, 101, 107,  94, 105, 122, 128,
+    120, 121, 113, 120, 118,  92, 114,  89,  60, 101, 102,  63,  99,  92, 109, 107,  90, 106, 121, 109,
+    126, 116,  71, 112, 118,  78, 119, 123, 110, 112, 116, 108,  99, 115, 114, 119, 126, 121, 125, 118,
+    112, 127, 119, 111, 129, 122, 111, 116, 116, 111,  78, 105, 101, 104,  65, 111, 120, 120, 111, 123,
+    124, 118, 108, 125, 124, 121,  95, 105, 125, 135, 123,  96,  99, 114, 118, 116, 117, 119, 115, 119,
+    123, 108, 123, 126, 118, 125,  70, 120, 116, 100, 108,  68,  78,  76,  86,  75,  87,  34,  81, 105,
+    114, 116,  75, 120, 125, 122, 101, 118, 119, 119, 104, 118, 122, 122, 120, 124, 111, 132, 121, 124,
+    113, 116, 128, 124, 129, 120, 108, 134, 111, 121, 120, 128, 127, 121, 103,  92, 117, 115, 113, 115,
+     86, 112, 121, 129, 125, 127, 121, 132, 118, 115, 116, 119, 123, 122, 112, 117, 111, 123, 133, 124,
+    133, 124, 123, 117, 130, 123, 121, 126, 127, 123, 126, 122, 124, 118, 121, 114,  89,  78,  80,  95,
+     99,  79,  68,  14,  80, 112, 129, 125, 112,  81,  54, 119, 126, 127, 130, 130, 123, 112, 110, 128,
+    128, 129, 134, 137, 127, 127, 130, 123, 111, 122, 130, 120, 128, 119, 111, 124, 132, 124, 115, 103,
+    111, 127, 126, 124, 125, 121,  98, 113, 127, 124, 124, 122, 125, 129, 125, 125, 115, 124, 130, 126,
+    125, 112, 107, 121, 135, 126, 126,  92,  50,  98, 118, 145, 134, 118,  61,  79, 123, 125, 131, 126,
+    109,  94,  86, 119, 111, 120, 118, 106, 112,  94, 114, 128, 122, 130, 128, 121, 124, 129, 113,  96,
+    106, 112, 125, 120, 117, 132, 127, 130, 110, 120, 119, 115, 126, 127, 123, 126, 120, 128, 126, 128,
+    137, 132, 130, 123,  99, 118, 133, 134, 136, 133, 131, 122,  96, 120, 133, 135, 136, 131, 130, 128,
+    123, 128, 122, 105, 119, 120, 122, 126, 129, 121, 124, 110, 107, 123, 120, 102, 116, 119, 107, 128,
+    131, 133, 139, 134, 130, 124,  83, 102, 114, 117, 124, 133, 124, 130, 118,  99, 110, 123, 122, 127,
+    133, 130, 130, 132, 130, 113, 119, 126, 134, 133, 136, 135, 127, 122, 121, 101,  54,  96, 125, 123,
+    128, 132, 121, 116, 123, 100,  58,  66,  90,  74, 107, 111, 116, 119, 117, 114, 103,  97,  73,  72,
+    103, 101, 128, 134, 118, 131, 121,  78, 105, 115, 129, 128, 135, 130, 124, 121, 122, 126, 128, 131,
+    120, 127, 130, 124, 125, 126, 128, 130, 132, 123, 122, 113, 119, 132, 131, 132, 120, 128, 134, 130,
+    108, 103, 120, 122, 117, 129, 124, 120, 130, 133, 129, 124, 128, 126, 122, 127, 121, 130, 134, 126,
+    123, 125, 127, 127, 125, 129, 137, 134, 144, 141, 129, 123, 110,  51,  95, 124, 135, 131, 147, 139,
+    135, 139, 126,  95,  64,  97, 108, 129, 129, 136, 138, 137, 130, 127, 121, 125, 125, 127, 130, 128,
+    130, 122, 124, 119, 127, 125, 126, 129, 130, 126, 126, 115, 124, 133, 121, 120, 100, 130, 126, 133,
+    135, 128, 131, 134, 135, 129, 115, 108, 113, 128, 124, 133, 134, 136, 128, 126, 133, 126, 129, 127,
+    126, 132, 129, 133, 131, 124, 125, 125, 122,  89, 108, 120, 121, 132, 125, 117, 112,  92,  89,  87,
+     78,  89,  94, 110, 128, 118, 102,  96,  99,  53,  50,  80,  97, 125, 125, 134, 141, 136, 132, 127,
+    126, 118, 106,  80,  99, 128, 124, 129, 134, 134, 133, 130, 129, 126, 128, 127, 129, 117, 125, 122,
+    105, 116, 127, 131, 127, 126, 124, 131, 125, 128, 134, 131, 122, 115, 119, 129, 128, 126, 132, 131,
+    118, 112, 113, 123, 117,  89, 112, 129, 131, 128, 123, 133, 122, 125, 122, 122, 120, 119, 123, 126,
+    124, 129, 124, 108, 127, 130, 135, 134, 132, 128, 131, 135, 132, 133, 131, 122, 116, 122, 129, 129,
+    127, 129, 128, 126, 112, 118, 117, 114, 118, 130, 126, 125, 127, 131, 128, 126, 119, 122, 126, 121,
+    122, 107, 112, 123, 113, 111, 116, 121, 118, 113, 126, 130, 131, 130, 125, 132, 129, 120,  94,  88,
+     86, 104, 111, 131, 135, 135, 139, 138, 138, 134, 127, 118,  88,  69, 102, 119, 131, 130, 128, 135,
+    134, 132, 128, 131, 122, 114, 115,  92, 110, 122, 123, 119, 120, 125, 128, 129, 125, 118, 121, 121,
+    125, 120, 113, 117, 121, 126, 127, 127, 126, 126, 133, 135, 134, 129, 124, 129, 125, 131, 130, 117,
+    116, 115,  79,  68,  94, 110, 112, 125, 122, 121, 112, 113, 121, 128, 127, 123, 114, 124, 117, 106,
+    104,  96, 111, 110, 113, 109, 115, 116, 124, 120, 127, 122, 123, 128, 132, 123, 125, 120, 126, 128,
+    127, 129, 128, 130, 133, 133, 127, 127, 128, 132, 132, 125, 112, 115, 124, 134, 133, 131, 129, 128,
+};
+
+constexpr int kWinSpanBwd = 8;
+constexpr int kWinSpanFwd = 64;
+
+inline int64_t pick_window(int64_t sub0, int64_t row_bytes, int span) {
+    if (row_bytes != 4096 || sub0 < kWinLo || sub0 >= kWinHi || span < 1) return sub0;
+    const int64_t last = sub0 + (sub0 + span - 1) / span;
+    int64_t best = sub0;
+    for (int64_t s = sub0 + 1; s <= last && s < kWinHi; ++s)
+        if (kWinRate[s - kWinLo] > kWinRate[best - kWinLo]) best = s;
+    return best;
+}
+
 // The N-1 gaps between sequences take N-1 of the window slots (one sequence,
 // the training step, uses every slot: all CUs of the round get work).
-inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, int tw) {
+// row_bytes = H * element size (the dy / y row); span: see pick_window.
+inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, int tw, int64_t row_bytes, int span) {
     const int64_t g = groups > 0 ? groups : 1;
     const int64_t gaps = N > 1 ? N - 1 : 0;
     const int64_t per_xcd = (int64_t)resident * LFM2SC_ROUNDS / kXcds / g;
@@ -318,6 +400,7 @@ inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, in
     int64_t sub = (total_T + denom - 1) / denom;
     if (sub < LFM2SC_SUB_MIN) sub = LFM2SC_SUB_MIN;
     if (sub > (1 << 24)) sub = 1 << 24;
+    sub = pick_window(sub, row_bytes, span);
     const int64_t gap = sub * tw;
     return Tiling{(int)sub, (total_T + gap - 1) / gap + gaps};
 }

@@ -385,7 +385,8 @@ static hipError_t prefill_k(PrefillArgs<E> a, hipStream_t s) {
     constexpr auto kernel = prefill_kernel<E, K, fwd_unroll<E>()>;
     static const int resident = resident_workgroups(kernel, LFM2SC_FWD_LDS);
     const int gy = WgLayout<LFM2SC_FWD_TW>::groups(a.H);
-    const Tiling t = ragged_tiling(a.total_T, a.N, gy, resident, LFM2SC_FWD_TW);
+    const Tiling t = ragged_tiling(a.total_T, a.N, gy, resident, LFM2SC_FWD_TW, (int64_t)a.H * (int64_t)sizeof(E),
+                                   kWinSpanFwd);
     a.sub = t.sub;
     a.ntiles = (int)t.ntiles;
     hipLaunchKernelGGL(kernel, dim3(pad_xcd(a.ntiles), gy), dim3(kThreads), LFM2SC_FWD_LDS, s, a);
