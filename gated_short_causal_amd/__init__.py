@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     Lfm2scError,
     abi_version,
     lfm2sc_backward,
+    lfm2sc_backward_noalloc,
     lfm2sc_backward_workspace_bytes,
     lfm2sc_commit_window,
     lfm2sc_conv_update,

@@ -29,6 +29,8 @@ SIGNATURES = {
     "lfm2sc_backward_workspace_bytes": (_size, [_int, _int, _int, _i64, _int]),
     "lfm2sc_backward": (_int, [_int, _int, _int, _vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64,
                                _vp, _vp, _i64, _vp, _vp, _vp, _vp, _size, _vp]),
+    "lfm2sc_backward_noalloc": (_int, [_int, _int, _int, _vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _i64, _i64, _vp,
+                                       _vp, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp]),
     "lfm2sc_fused_prefill_workspace_bytes": (_size, [_int, _int, _int, _int, _int]),
     "lfm2sc_fused_prefill_plan": (_int, [_int, _int, _int, _i64]),
     "lfm2sc_fused_prefill": (_int, [_int, _int, _int, _int, _vp, _i64, _i64, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64,

@@ -269,6 +269,26 @@ def lfm2sc_backward(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, workspace,
     return d_in_proj, dW
 
 
+# LFM2SC_NOALLOC_SCRATCH_BYTES of include/lfm2sc.h: the most workspace lfm2sc_backward_noalloc can stand in for
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def lfm2sc_backward_noalloc(in_proj, cu_seqlens, weight, dy, d_in_proj, dW, init_state_pool=None, slot_idx=None,
+                            bias=None, d_final_state=None, dbias=None, d_init_state=None):
+    """lfm2sc_backward without a workspace argument, for callers that cannot allocate: the library keeps the
+    partial sums in a fixed device array of NOALLOC_SCRATCH_BYTES per GPU.  Calls that overlap on one GPU race."""
+    H, K, N, T, num_slots, slot_stride, (in_s, dy_s, din_s) = _backward_args(
+        in_proj, cu_seqlens, weight, dy, d_in_proj, dW, None, init_state_pool, slot_idx, bias, d_final_state,
+        dbias, d_init_state)
+    _check(_lib.lib().lfm2sc_backward_noalloc(
+        _dtype_code(weight), H, K, _ptr(in_proj), in_s, T,
+        _ptr(cu_seqlens), N, _ptr(weight), _ptr(bias),
+        _ptr(init_state_pool), num_slots, slot_stride, _ptr(slot_idx),
+        _ptr(dy), dy_s, _ptr(d_final_state), _ptr(d_in_proj), din_s, _ptr(dW),
+        _ptr(dbias), _ptr(d_init_state), _stream(weight.device)))
+    return d_in_proj, dW
+
+
 def lfm2sc_fused_prefill_workspace_bytes(dtype, H, K, num_seqs, with_pool) -> int:
     code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(_lib.lib().lfm2sc_fused_prefill_workspace_bytes(code, H, K, num_seqs, int(bool(with_pool))))

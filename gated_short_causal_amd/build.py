@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblfm2sc.so")
-SOURCES = ["fwd.hip", "bwd.hip", "fused.hip", "fused_split.hip", "interop.hip", "check.hip", "api.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "fused.hip", "fused_split.hip", "interop.hip", "check.hip", "noalloc.hip", "api.cpp"]
 
 
 def hipcc() -> str:

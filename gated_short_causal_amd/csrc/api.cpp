@@ -162,7 +162,7 @@ int commit_impl(int H, int K, const void* windows, int N, int L, const int32_t* 
 }
 
 template <typename E>
-int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T, const int32_t* cu, int N,
+int backward_impl(const char* fn, int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T, const int32_t* cu, int N,
                   const void* weight, const void* bias, const void* pool, int64_t num_slots, int64_t slot_stride,
                   const int32_t* slot_idx, const void* dy, int64_t dy_stride, const void* dfinal, void* din,
                   int64_t din_stride, float* dW, float* dbias, void* dinit, void* ws, hipStream_t s) {
@@ -180,7 +180,7 @@ int backward_impl(int H, int K, const void* in_proj, int64_t in_stride, int64_t 
     a.H = H;
     a.sub = 0;
     a.ntiles = 0;
-    return launched("lfm2sc_backward", launch_backward<E>(a, K, s));
+    return launched(fn, launch_backward<E>(a, K, s));
 }
 
 size_t workspace_bytes(int dtype, int H, int K, int64_t total_T, int N) {
@@ -188,6 +188,73 @@ size_t workspace_bytes(int dtype, int H, int K, int64_t total_T, int N) {
     const int64_t nt = backward_partial_rows(dtype == LFM2SC_F32, H, K, total_T, N);
     const size_t bytes = (size_t)nt * (size_t)H * (size_t)(K + 1) * (size_t)backward_partial_bytes(dtype == LFM2SC_F32);
     return (bytes + 255) / 256 * 256;
+}
+
+// lfm2sc_backward and lfm2sc_backward_noalloc: the same validation; the second takes its workspace from the
+// library's fixed device array instead of the caller.
+int backward_entry(const char* fn, int dtype, int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T,
+                   const int32_t* cu_seqlens, int num_seqs, const void* weight, const void* bias,
+                   const void* init_state_pool, int64_t num_slots, int64_t slot_stride, const int32_t* slot_idx,
+                   const void* dy, int64_t dy_stride, const void* d_final_state, void* d_in_proj, int64_t din_stride,
+                   float* dW, float* dbias, void* d_init_state, void* workspace, size_t workspace_bytes_, bool noalloc,
+                   void* stream) {
+    TRY(check_common(fn, dtype, H, K, bias));
+    if (num_seqs < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d is negative", fn, num_seqs);
+    if (total_T < 0 || total_T >= kMaxRows)
+        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: total_T=%lld outside [0, 2^31)", fn, (long long)total_T);
+    TRY(check_stride(fn, "in_stride", in_stride, 3 * (int64_t)H));
+    TRY(check_stride(fn, "dy_stride", dy_stride, H));
+    TRY(check_stride(fn, "din_stride", din_stride, 3 * (int64_t)H));
+    TRY(check_ptr(fn, "dW", dW, 4));
+    if (dbias != nullptr && !aligned(dbias, 4)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: dbias is not 4-byte aligned", fn);
+    if (d_final_state != nullptr && !aligned(d_final_state, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_final_state is not 16-byte aligned", fn);
+    if (d_init_state != nullptr && !aligned(d_init_state, 16))
+        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_init_state is not 16-byte aligned", fn);
+    const bool work = num_seqs > 0 && total_T > 0;
+    if (num_seqs > 0) TRY(check_ptr(fn, "cu_seqlens", cu_seqlens, 4));
+    if (work) {
+        TRY(check_ptr(fn, "in_proj", in_proj, 16));
+        TRY(check_ptr(fn, "weight", weight, 16));
+        TRY(check_ptr(fn, "dy", dy, 16));
+        TRY(check_ptr(fn, "d_in_proj", d_in_proj, 16));
+        if (init_state_pool != nullptr)
+            TRY(check_pool(fn, init_state_pool, num_slots, slot_stride, slot_idx, H, K));
+        if (ragged_tiles_bound(total_T, num_seqs) >= (1 << 30))
+            return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many sequences/tokens for one launch", fn);
+        const size_t need = workspace_bytes(dtype, H, K, total_T, num_seqs);
+        if (noalloc) {
+            if (need > noalloc_scratch_bytes())
+                return fail(LFM2SC_ERR_WORKSPACE,
+                            "%s: this call needs %zu bytes of workspace; the no-alloc entry point holds %zu "
+                            "(LFM2SC_NOALLOC_SCRATCH_BYTES): use lfm2sc_backward with a caller workspace",
+                            fn, need, noalloc_scratch_bytes());
+        } else {
+            if (workspace == nullptr || workspace_bytes_ < need)
+                return fail(LFM2SC_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace,
+                            workspace_bytes_, need);
+            if (!aligned(workspace, 16))
+                return fail(LFM2SC_ERR_ALIGNMENT, "%s: workspace is not 16-byte aligned", fn);
+        }
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (noalloc && work) {
+        const hipError_t e = noalloc_scratch(s, &workspace);
+        if (e != hipSuccess) return launched(fn, e);
+    }
+    if (num_seqs > 0)
+        TRY(device_check(fn, s, (work && init_state_pool) ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens,
+                         total_T, nullptr, 0));
+    // With no token the launch still runs the reduction over zero windows (dW = 0, dbias = 0) and, when asked,
+    // writes d_init_state = d_final_state (or 0) for every (empty) sequence.
+    const int64_t T_eff = work ? total_T : 0;
+    if (dtype == LFM2SC_BF16)
+        return backward_impl<uint16_t>(fn, H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias,
+                                       init_state_pool, num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state,
+                                       d_in_proj, din_stride, dW, dbias, d_init_state, workspace, s);
+    return backward_impl<float>(fn, H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias, init_state_pool,
+                                num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state, d_in_proj, din_stride,
+                                dW, dbias, d_init_state, workspace, s);
 }
 
 }  // namespace
@@ -320,51 +387,20 @@ int lfm2sc_backward(int dtype, int H, int K, const void* in_proj, int64_t in_str
                     const void* dy, int64_t dy_stride, const void* d_final_state, void* d_in_proj, int64_t din_stride,
                     float* dW, float* dbias, void* d_init_state, void* workspace, size_t workspace_bytes_,
                     void* stream) {
-    const char* fn = "lfm2sc_backward";
-    TRY(check_common(fn, dtype, H, K, bias));
-    if (num_seqs < 0) return fail(LFM2SC_ERR_BAD_SHAPE, "%s: num_seqs=%d is negative", fn, num_seqs);
-    if (total_T < 0 || total_T >= kMaxRows)
-        return fail(LFM2SC_ERR_BAD_SHAPE, "%s: total_T=%lld outside [0, 2^31)", fn, (long long)total_T);
-    TRY(check_stride(fn, "in_stride", in_stride, 3 * (int64_t)H));
-    TRY(check_stride(fn, "dy_stride", dy_stride, H));
-    TRY(check_stride(fn, "din_stride", din_stride, 3 * (int64_t)H));
-    TRY(check_ptr(fn, "dW", dW, 4));
-    if (dbias != nullptr && !aligned(dbias, 4)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: dbias is not 4-byte aligned", fn);
-    if (d_final_state != nullptr && !aligned(d_final_state, 16))
-        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_final_state is not 16-byte aligned", fn);
-    if (d_init_state != nullptr && !aligned(d_init_state, 16))
-        return fail(LFM2SC_ERR_ALIGNMENT, "%s: d_init_state is not 16-byte aligned", fn);
-    const bool work = num_seqs > 0 && total_T > 0;
-    if (num_seqs > 0) TRY(check_ptr(fn, "cu_seqlens", cu_seqlens, 4));
-    if (work) {
-        TRY(check_ptr(fn, "in_proj", in_proj, 16));
-        TRY(check_ptr(fn, "weight", weight, 16));
-        TRY(check_ptr(fn, "dy", dy, 16));
-        TRY(check_ptr(fn, "d_in_proj", d_in_proj, 16));
-        if (init_state_pool != nullptr)
-            TRY(check_pool(fn, init_state_pool, num_slots, slot_stride, slot_idx, H, K));
-        if (ragged_tiles_bound(total_T, num_seqs) >= (1 << 30))
-            return fail(LFM2SC_ERR_BAD_SHAPE, "%s: too many sequences/tokens for one launch", fn);
-        const size_t need = workspace_bytes(dtype, H, K, total_T, num_seqs);
-        if (workspace == nullptr || workspace_bytes_ < need)
-            return fail(LFM2SC_ERR_WORKSPACE, "%s: workspace %p of %zu bytes, %zu needed", fn, workspace,
-                        workspace_bytes_, need);
-        if (!aligned(workspace, 16)) return fail(LFM2SC_ERR_ALIGNMENT, "%s: workspace is not 16-byte aligned", fn);
-    }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (num_seqs > 0)
-        TRY(device_check(fn, s, (work && init_state_pool) ? slot_idx : nullptr, num_seqs, num_slots, cu_seqlens,
-                         total_T, nullptr, 0));
-    // With no token the launch still runs the reduction over zero windows (dW = 0, dbias = 0) and, when asked,
-    // writes d_init_state = d_final_state (or 0) for every (empty) sequence.
-    const int64_t T_eff = work ? total_T : 0;
-    if (dtype == LFM2SC_BF16)
-        return backward_impl<uint16_t>(H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias,
-                                       init_state_pool, num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state,
-                                       d_in_proj, din_stride, dW, dbias, d_init_state, workspace, s);
-    return backward_impl<float>(H, K, in_proj, in_stride, T_eff, cu_seqlens, num_seqs, weight, bias, init_state_pool,
-                                num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state, d_in_proj, din_stride,
-                                dW, dbias, d_init_state, workspace, s);
+    return backward_entry("lfm2sc_backward", dtype, H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs, weight,
+                          bias, init_state_pool, num_slots, slot_stride, slot_idx, dy, dy_stride, d_final_state,
+                          d_in_proj, din_stride, dW, dbias, d_init_state, workspace, workspace_bytes_, false, stream);
+}
+
+int lfm2sc_backward_noalloc(int dtype, int H, int K, const void* in_proj, int64_t in_stride, int64_t total_T,
+                            const int32_t* cu_seqlens, int num_seqs, const void* weight, const void* bias,
+                            const void* init_state_pool, int64_t num_slots, int64_t slot_stride,
+                            const int32_t* slot_idx, const void* dy, int64_t dy_stride, const void* d_final_state,
+                            void* d_in_proj, int64_t din_stride, float* dW, float* dbias, void* d_init_state,
+                            void* stream) {
+    return backward_entry("lfm2sc_backward_noalloc", dtype, H, K, in_proj, in_stride, total_T, cu_seqlens, num_seqs,
+                          weight, bias, init_state_pool, num_slots, slot_stride, slot_idx, dy, dy_stride,
+                          d_final_state, d_in_proj, din_stride, dW, dbias, d_init_state, nullptr, 0, true, stream);
 }
 
 int lfm2sc_conv_update(int dtype, int H, int K, int num_seqs, int L, const void* bx, int64_t bx_stride_n,

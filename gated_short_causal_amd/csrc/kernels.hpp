@@ -118,6 +118,11 @@ template <typename E> hipError_t launch_verify(const VerifyArgs<E>& a, int K, hi
 template <typename E> hipError_t launch_commit(const CommitArgs<E>& a, int K, hipStream_t s);
 template <typename E> hipError_t launch_backward(const BackwardArgs<E>& a, int K, hipStream_t s);
 
+// The fixed device array behind lfm2sc_backward_noalloc: its size, and its
+// address on the device of `stream` (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 // Debug precondition checks (LFM2SC_CHECK=1).  Each returns 0 when the device
 // data satisfies the precondition, a nonzero mask otherwise; synchronises `s`.
 enum CheckBits { kBadSlotRange = 1, kDupSlot = 2, kBadCu = 4, kBadAccept = 8 };

@@ -13,8 +13,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers unless stated otherwise; the caller
- *    owns every buffer.  The library allocates no device memory, keeps no
- *    device state between calls and is safe to call from several host threads.
+ *    owns every buffer.  The library allocates no device memory and keeps no
+ *    device state between calls (lfm2sc_backward_noalloc's fixed scratch array
+ *    aside), and is safe to call from several host threads.
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*, NULL =
  *    the null stream).  The return code covers host-side argument checks and
  *    launch errors only; a fault inside a kernel surfaces at the caller's next
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LFM2SC_ABI_VERSION 5
+#define LFM2SC_ABI_VERSION 6
 
 enum lfm2sc_dtype { LFM2SC_BF16 = 0, LFM2SC_F32 = 1 };
 
@@ -224,6 +225,37 @@ int lfm2sc_backward(int dtype, int H, int K,
                     float* dW, float* dbias,
                     void* d_init_state,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lfm2sc_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and determinism as lfm2sc_backward,
+ * without the workspace: the per-window partial sums live in a fixed array of
+ * LFM2SC_NOALLOC_SCRATCH_BYTES in device memory that the library holds on each
+ * GPU it runs on until the process ends (its address is looked up once per
+ * device on the first call there).  The call itself allocates nothing.
+ *
+ * Limit: the call must need at most LFM2SC_NOALLOC_SCRATCH_BYTES of workspace,
+ * i.e. lfm2sc_backward_workspace_bytes(...) <= LFM2SC_NOALLOC_SCRATCH_BYTES
+ * (one 65,536-token sequence at H = 2048 needs 2 MiB; the workspace grows with
+ * the number of sequences); a larger call returns LFM2SC_ERR_WORKSPACE before
+ * any launch.  Every call on one GPU uses that GPU's one array: calls that
+ * overlap on a GPU (other streams or host threads without ordering) race and
+ * may return wrong dW / dbias.  Nothing in the array needs clearing between
+ * calls (each call writes all of what it reads).
+ */
+#define LFM2SC_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int lfm2sc_backward_noalloc(int dtype, int H, int K,
+                            const void* in_proj, int64_t in_stride, int64_t total_T,
+                            const int32_t* cu_seqlens, int num_seqs,
+                            const void* weight, const void* bias,
+                            const void* init_state_pool, int64_t num_slots, int64_t slot_stride,
+                            const int32_t* slot_idx,
+                            const void* dy, int64_t dy_stride,
+                            const void* d_final_state,
+                            void* d_in_proj, int64_t din_stride,
+                            float* dW, float* dbias,
+                            void* d_init_state, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* lfm2sc_status_string(int status);

@@ -33,7 +33,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
     for n in names:
         assert hasattr(L, n), n
@@ -258,3 +258,40 @@ def test_conv_update_no_work_is_ok(L):
     assert _cu(L, N=0, bx=None, out=None, pool=None, slot_idx=None) == OK
     assert _cu(L, L=0, bx=None, out=None, pool=None, slot_idx=None) == OK
 
+
+
+def _bwd_noalloc(L, **kw):
+    a = dict(dtype=0, H=2048, K=3, in_proj=P, in_stride=6144, total_T=65536, cu=P, N=1, w=P, bias=None, pool=None,
+             num_slots=0, slot_stride=0, slot_idx=None, dy=P, dy_stride=2048, dF=None, din=P, din_stride=6144, dW=P,
+             dbias=None, dinit=None, stream=None)
+    a.update(kw)
+    return L.lfm2sc_backward_noalloc(a["dtype"], a["H"], a["K"], a["in_proj"], a["in_stride"], a["total_T"], a["cu"],
+                                     a["N"], a["w"], a["bias"], a["pool"], a["num_slots"], a["slot_stride"],
+                                     a["slot_idx"], a["dy"], a["dy_stride"], a["dF"], a["din"], a["din_stride"],
+                                     a["dW"], a["dbias"], a["dinit"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(din=None), NULLP), (dict(dW=None), NULLP), (dict(H=12), SHAPE), (dict(dy_stride=2040), SHAPE),
+    (dict(din_stride=6150), ALIGN), (dict(dtype=3), UNSUP), (dict(in_proj=MIS), ALIGN),
+    # more windows than the fixed scratch array holds partial rows for
+    (dict(N=5000, total_T=1 << 20), WS), (dict(H=131072, total_T=1 << 20, in_stride=3 * 131072,
+                                                dy_stride=131072, din_stride=3 * 131072), WS),
+])
+def test_backward_noalloc_rejects(L, kw, code):
+    assert _bwd_noalloc(L, **kw) == code
+    if code == WS:
+        assert b"LFM2SC_NOALLOC_SCRATCH_BYTES" in L.lfm2sc_last_error()
+
+
+def test_noalloc_limit_matches_header():
+    from gated_short_causal_amd import binding
+    m = re.search(r"#define\s+LFM2SC_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", open(HEADER).read())
+    assert m and binding.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_headline_call_fits(L):
+    """One 65,536-token sequence at H=2048 (the training step) fits the fixed scratch array."""
+    from gated_short_causal_amd import binding
+    need = L.lfm2sc_backward_workspace_bytes(0, 2048, 3, 65536, 1)
+    assert 0 < need <= binding.NOALLOC_SCRATCH_BYTES
