@@ -271,7 +271,7 @@ def graph_time(calls, replays):
     return t0.elapsed_time(t1) / (replays * len(calls))
 
 
-def extra_measurements(wl_mod, steps):
+def extra_measurements(wl_mod, steps, fused=True):
     """Decode, ragged prefill and verify at their LFM2-1.2B shapes.  Input sets are rotated so that one pass
     touches more than 2 x 256 MB (past the Infinity Cache): these are HBM figures.  `ms` is GPU time per call
     from graph replay; `eager_ms` is the back-to-back eager rate, which includes host launch overhead."""
@@ -332,8 +332,9 @@ def extra_measurements(wl_mod, steps):
         record(f"conv_update_64x8_{kind}", calls, algo_bytes_conv_update(64, 8, 2048, 3, 2))
         del sets, bxs, outs, tapes, calls
     out.update(train_t4096_measurement(wl_mod, steps))
-    out.update(fused_measurements(wl_mod, steps))
-    out.update(shape_measurements(wl_mod, steps))
+    if fused:
+        out.update(fused_measurements(wl_mod, steps))
+        out.update(shape_measurements(wl_mod, steps))
     return out
 
 
@@ -493,6 +494,8 @@ def main():
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the decode, ragged prefill and verify figures (graph replay, a few seconds)")
     ap.add_argument("--extra", dest="extra", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--no-fused", dest="fused", action="store_false",
+                    help="in the extra figures, skip the fused forward and the other-shape training steps")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--fused-only", action="store_true",
                     help="only the fused in_proj + ShortConv training forward (y only), for counter passes")
@@ -602,7 +605,7 @@ def main():
     cc["backward_frac"] = round(bwd_gbs / cc["GB/s"], 4)
     line["copy_ceiling"] = cc
     if args.extra:
-        line["extra"] = extra_measurements(wl, max(2, args.steps // 2))
+        line["extra"] = extra_measurements(wl, max(2, args.steps // 2), args.fused)
     if not args.no_cpu:
         print("bench: timing the oracle CPU baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(wl, T, H, K, args.cpu_channels)
