@@ -16,7 +16,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# LFM2SC_ORACLE_LIB may name another build of the same source (the sanitizer build of the host tests).
+_LIB_PATH = os.environ.get("LFM2SC_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _dp = ctypes.POINTER(ctypes.c_double)
