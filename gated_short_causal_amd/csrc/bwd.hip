@@ -512,8 +512,10 @@ template <typename E, int K> constexpr int bwd_unroll() {
 template <typename E, int K>
 static Tiling backward_tiling(int64_t total_T, int N, int H) {
     constexpr auto kernel = backward_kernel<E, K, bwd_unroll<E, K>()>;
-    static const int resident = resident_workgroups(kernel, bwd_dyn_lds<E, K>());
-    return ragged_tiling(total_T, N, WgLayout<LFM2SC_BWD_TW>::groups(H), resident, LFM2SC_BWD_TW,
+    static const int resident_long = resident_workgroups(kernel, bwd_dyn_lds<E, K>());
+    static const int resident_short = resident_workgroups(kernel, 0);
+    return ragged_tiling(total_T, N, WgLayout<LFM2SC_BWD_TW>::groups(H),
+                         total_T < LFM2SC_SHORT_T ? resident_short : resident_long, LFM2SC_BWD_TW,
                          (int64_t)H * (int64_t)sizeof(E), kWinSpanBwd);
 }
 
@@ -525,7 +527,7 @@ static hipError_t backward_k(BackwardArgs<E> a, hipStream_t s) {
         a.sub = t.sub;
         a.ntiles = (int)t.ntiles;
         const int gy = WgLayout<LFM2SC_BWD_TW>::groups(a.H);
-        const size_t dyn_lds = bwd_dyn_lds<E, K>();
+        const size_t dyn_lds = a.total_T < LFM2SC_SHORT_T ? 0 : bwd_dyn_lds<E, K>();
         hipLaunchKernelGGL((backward_kernel<E, K, bwd_unroll<E, K>()>), dim3(pad_xcd(a.ntiles), gy), dim3(kThreads),
                            dyn_lds, s, a);
         const hipError_t e = hipGetLastError();

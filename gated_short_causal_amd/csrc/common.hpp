@@ -42,11 +42,20 @@
 #ifndef LFM2SC_BWD_LDS
 #define LFM2SC_BWD_LDS 82944   // same for the backward (its static LDS stays within 160 KiB with it)
 #endif
+#ifndef LFM2SC_SHORT_T
+#define LFM2SC_SHORT_T 0       // ragged calls with fewer tokens than this launch without the LDS reservation
+#endif                         // (several workgroups per CU, shorter windows); 0 = never
 #ifndef LFM2SC_BWD_U
 #define LFM2SC_BWD_U 3         // token rows of loads in flight per wave (backward, bf16 I/O)
 #endif
 #ifndef LFM2SC_FWD_NT
 #define LFM2SC_FWD_NT 1        // non-temporal hints on streamed rows, forward: 1 = loads, 2 = stores, 3 = both
+#endif
+#ifndef LFM2SC_DEC_NT
+#define LFM2SC_DEC_NT 0        // non-temporal hints in decode (bits): 1 in_proj loads, 2 y stores, 4 state loads,
+#endif                         // 8 state stores
+#ifndef LFM2SC_VER_NT
+#define LFM2SC_VER_NT 0        // same for verify: 1 in_proj loads, 2 y stores, 4 state loads, 8 tape stores
 #endif
 #ifndef LFM2SC_BWD_NT
 #define LFM2SC_BWD_NT 3        // same for the backward
@@ -180,6 +189,29 @@ __device__ __forceinline__ void load_block(const E* p, float (&s)[kChPerLane][K]
     for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int k = 0; k < K; ++k) s[c][k] = f[c * K + k];
+}
+
+// The same with non-temporal hints (NT bit 1: loads, bit 2: stores, as ld8s / st8s).
+template <typename E, int K, int NT>
+__device__ __forceinline__ void load_block_s(const E* p, float (&s)[kChPerLane][K]) {
+    float f[8 * K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) to_f32(ld8s<E, NT>(p + 8 * j), f + 8 * j);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) s[c][k] = f[c * K + k];
+}
+
+template <typename E, int K, int NT>
+__device__ __forceinline__ void store_block_s(E* p, const float (&s)[kChPerLane][K]) {
+    float f[8 * K];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) f[c * K + k] = s[c][k];
+#pragma unroll
+    for (int j = 0; j < K; ++j) st8s<E, NT>(p + 8 * j, from_f32<E>(f + 8 * j));
 }
 
 template <typename E, int K>

@@ -238,7 +238,8 @@ __device__ __forceinline__ void decode_one(const DecodeArgs<E>& a, int i, int g)
     const int64_t slot = a.slot_idx[i];
     const bool ok = slot_ok(slot, a.num_slots);
     const E* row = a.in + (int64_t)i * a.in_stride + ch0;
-    const Raw8<E> rb = ld8<E>(row), rc = ld8<E>(row + H), rx = ld8<E>(row + 2 * H);
+    const Raw8<E> rb = ld8s<E, LFM2SC_DEC_NT>(row), rc = ld8s<E, LFM2SC_DEC_NT>(row + H),
+                  rx = ld8s<E, LFM2SC_DEC_NT>(row + 2 * H);
     float wf[kChPerLane][K];
     load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
     float bv[kChPerLane] = {};
@@ -246,7 +247,7 @@ __device__ __forceinline__ void decode_one(const DecodeArgs<E>& a, int i, int g)
     E* sp = ok ? a.pool + slot * a.slot_stride + (int64_t)ch0 * K : nullptr;
     float s[kChPerLane][K];
     if (ok) {
-        load_block<E, K>(sp, s);
+        load_block_s<E, K, (LFM2SC_DEC_NT & 4) ? 1 : 0>(sp, s);
     } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -265,8 +266,8 @@ __device__ __forceinline__ void decode_one(const DecodeArgs<E>& a, int i, int g)
         for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
         yv[c] = c8[c] * conv;
     }
-    store_f32x8<E>(a.y + (int64_t)i * a.y_stride + ch0, yv);
-    if (ok) store_block<E, K>(sp, s);
+    store_f32x8s<E, LFM2SC_DEC_NT>(a.y + (int64_t)i * a.y_stride + ch0, yv);
+    if (ok) store_block_s<E, K, (LFM2SC_DEC_NT & 8) ? 2 : 0>(sp, s);
 }
 
 template <typename E, int K>
@@ -306,7 +307,7 @@ __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g,
         const int t = s0 + k - K;                      // token whose bx is window entry k
         if (t >= 0) {
             const E* row = base + (int64_t)t * a.in_stride;
-            hb[k - 1] = ld8<E>(row); hx[k - 1] = ld8<E>(row + 2 * H);
+            hb[k - 1] = ld8s<E, LFM2SC_VER_NT>(row); hx[k - 1] = ld8s<E, LFM2SC_VER_NT>(row + 2 * H);
         }
     }
     Raw8<E> rb[U], rc[U], rx[U];
@@ -314,7 +315,8 @@ __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g,
     for (int u = 0; u < U; ++u) {
         if (u < n) {
             const E* row = base + (int64_t)(s0 + u) * a.in_stride;
-            rb[u] = ld8<E>(row); rc[u] = ld8<E>(row + H); rx[u] = ld8<E>(row + 2 * H);
+            rb[u] = ld8s<E, LFM2SC_VER_NT>(row); rc[u] = ld8s<E, LFM2SC_VER_NT>(row + H);
+            rx[u] = ld8s<E, LFM2SC_VER_NT>(row + 2 * H);
         }
     }
     float st[kChPerLane][K];
@@ -322,7 +324,7 @@ __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g,
     if (need_state) {
         const int64_t slot = a.slot_idx[i];
         if (slot_ok(slot, a.num_slots)) {
-            load_block<E, K>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, st);
+            load_block_s<E, K, (LFM2SC_VER_NT & 4) ? 1 : 0>(a.pool + slot * a.slot_stride + (int64_t)ch0 * K, st);
         } else {
 #pragma unroll
             for (int c = 0; c < 8; ++c)
@@ -375,8 +377,8 @@ __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g,
                 for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
                 yv[c] = c8[c] * conv;
             }
-            store_f32x8<E>(ybase + (int64_t)(s0 + u) * a.y_stride, yv);
-            store_block<E, K>(tbase + (int64_t)(s0 + u) * HK, s);
+            store_f32x8s<E, LFM2SC_VER_NT>(ybase + (int64_t)(s0 + u) * a.y_stride, yv);
+            store_block_s<E, K, (LFM2SC_VER_NT & 8) ? 2 : 0>(tbase + (int64_t)(s0 + u) * HK, s);
         }
     }
 }

@@ -302,6 +302,16 @@ const char* lfm2sc_last_error(void);
  * (0: never split or mid tiles, 1: always, 32 or 64: split tiles with that
  * many channels, 128: mid tiles), LFM2SC_FUSED_HALO (0 or 1) and
  * LFM2SC_FUSED_WIDE (0: the 4-wave tile instead of the wide one) force one.
+ * When to call it (measured on MI355X, D = H = 2048, K = 3, against a bf16
+ * library GEMM into in_proj followed by lfm2sc_prefill_ragged): the fused call
+ * is faster for short inputs (T <= 256, and 256 one-token sequences with a
+ * pool: 20-55%) and for long forward-only inputs (T = 65,536 with y only: 5%),
+ * level around T = 1,024 and T = 4,096, and slower between T ~ 1,280 and
+ * 2,048 (12-34%), at T = 512-768 (4-7%), on a ragged batch of 8 sequences of
+ * 64-2,048 tokens (~12%) and when in_proj_out is also wanted for the backward
+ * (~7% at T = 65,536).  Callers should take the two-step path for those
+ * shapes; the call does not switch to it by itself (it never runs a library
+ * GEMM).
  */
 int lfm2sc_fused_prefill(int dtype, int H, int K, int D,
                          const void* x, int64_t x_stride, int64_t total_T,
