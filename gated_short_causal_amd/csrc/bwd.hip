@@ -373,6 +373,7 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     const int ch0 = ((blockIdx.y * Lay::kCW + wave / TW) * kWave + lane) * kChPerLane;
     const bool lane_on = tile < a.ntiles && ch0 < a.H;
+    const bool tile_on = tile < a.ntiles;   // wave-uniform
 
     BwdState<E, K> st;
 #pragma unroll
@@ -383,11 +384,12 @@ __global__ __launch_bounds__(kThreads) void backward_kernel(const BackwardArgs<E
         for (int k = 0; k < PC; ++k) st.acc[c][k] = (A)0;
     }
 
-    if (lane_on) {
+    if (tile_on) {
         const int64_t gap = (int64_t)a.sub * TW;
         const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % TW) * a.sub;
         SeqSpan sp;
-        if (find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) {
+        // the span search runs with every lane of the wave active; lanes past H then stay idle
+        if (find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp) && lane_on) {
             float wf[kChPerLane][K];
             load_block<E, K>(a.w + (int64_t)ch0 * K, wf);
             float bv[8] = {};

@@ -58,11 +58,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> 
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
     const int ch0 = ((blockIdx.y * Lay::kCW + wave / LFM2SC_FWD_TW) * kWave + lane) * kChPerLane;
-    if (ch0 >= a.H) return;
     const int64_t gap = (int64_t)a.sub * LFM2SC_FWD_TW;
     const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % LFM2SC_FWD_TW) * a.sub;
     SeqSpan sp;
-    if (!find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) return;
+    if (!find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) return;   // all lanes still active here
+    if (ch0 >= a.H) return;
     int64_t lo = sp.lo, hi = sp.hi;
     const bool owner = (lo == 0);
     if (owner) {
