@@ -57,6 +57,10 @@
 #ifndef LFM2SC_VER_NT
 #define LFM2SC_VER_NT 11       // same for verify: 1 in_proj loads, 2 y stores, 4 state loads, 8 tape stores.
 #endif                         // Measured at 64 x 8: 0 -> 6.24 us, 2 -> 6.10, 10 -> 5.95, 11 -> 5.89
+#ifndef LFM2SC_CVU_NT
+#define LFM2SC_CVU_NT 3        // same for the interop conv update (vector layouts): 1 bx loads, 2 out stores,
+#endif                         // 8 tape stores.  Measured at 64 x 8 (view / dense): 0 -> 6.25 / 6.56 us,
+                               // 3 -> 5.83 / 6.02, 11 -> 6.48 / 6.00
 #ifndef LFM2SC_BWD_NT
 #define LFM2SC_BWD_NT 3        // same for the backward
 #endif

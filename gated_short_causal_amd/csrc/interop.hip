@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_kernel(const ConvUpda
             if (u < n) {
                 const E* p = bxi + (int64_t)(t0 + u) * a.bx_st;
                 if constexpr (VEC) {
-                    load_f32x8<E>(p, x[u]);
+                    to_f32(ld8s<E, LFM2SC_CVU_NT>(p), x[u]);
                 } else {
 #pragma unroll
                     for (int c = 0; c < 8; ++c) x[u][c] = ld1<E>(p + (int64_t)c * a.bx_sh);
@@ -90,13 +90,14 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_kernel(const ConvUpda
                 }
                 E* q = oi + (int64_t)(t0 + u) * a.out_st;
                 if constexpr (VEC) {
-                    store_f32x8<E>(q, y);
+                    store_f32x8s<E, LFM2SC_CVU_NT>(q, y);
                 } else {
 #pragma unroll
                     for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
                 }
                 if (a.win != nullptr)
-                    store_block<E, K>(a.win + (((int64_t)i * a.L + t0 + u) * a.H + ch0) * K, s);
+                    store_block_s<E, K, (LFM2SC_CVU_NT & 8) ? 2 : 0>(a.win + (((int64_t)i * a.L + t0 + u) * a.H + ch0) * K,
+                                                                    s);
             }
         }
     }
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const Con
     auto load_bx = [&](int t, float* x) {
         const E* p = bxi + (int64_t)t * a.bx_st;
         if constexpr (VEC) {
-            load_f32x8<E>(p, x);
+            to_f32(ld8s<E, LFM2SC_CVU_NT>(p), x);
         } else {
 #pragma unroll
             for (int c = 0; c < 8; ++c) x[c] = ld1<E>(p + (int64_t)c * a.bx_sh);
@@ -170,12 +171,12 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const Con
     }
     E* q = a.out + (int64_t)i * a.out_sn + (int64_t)ch0 * a.out_sh + (int64_t)t0 * a.out_st;
     if constexpr (VEC) {
-        store_f32x8<E>(q, y);
+        store_f32x8s<E, LFM2SC_CVU_NT>(q, y);
     } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
     }
-    store_block<E, K>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
+    store_block_s<E, K, (LFM2SC_CVU_NT & 8) ? 2 : 0>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
 }
 
 // Token stride 1: one lane per channel, all L steps of the sequence in the
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const Con
         const int n = a.L - t0 < 8 ? a.L - t0 : 8;
         float x[8], y[8];
         if constexpr (VEC) {
-            load_f32x8<E>(xb + t0, x);
+            to_f32(ld8s<E, LFM2SC_CVU_NT>(xb + t0), x);
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u) x[u] = u < n ? ld1<E>(xb + t0 + u) : 0.f;
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const Con
             }
         }
         if constexpr (VEC) {
-            store_f32x8<E>(ob + t0, y);
+            store_f32x8s<E, LFM2SC_CVU_NT>(ob + t0, y);
         } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u)
