@@ -45,6 +45,9 @@
 #ifndef LFM2SC_SHORT_T
 #define LFM2SC_SHORT_T 0       // ragged calls with fewer tokens than this launch without the LDS reservation
 #endif                         // (several workgroups per CU, shorter windows); 0 = never
+#ifndef LFM2SC_WIN_TABLES
+#define LFM2SC_WIN_TABLES 1    // 1: window lengths from the measured rate tables below; 0: always the shortest
+#endif                         // window that fits one round (the setting those tables are measured with)
 #ifndef LFM2SC_BWD_U
 #define LFM2SC_BWD_U 3         // token rows of loads in flight per wave (backward, bf16 I/O)
 #endif
@@ -369,80 +372,195 @@ struct WgLayout {
 // their rows a fixed `sub` apart, so the HBM channels and banks that serve
 // them at any moment follow from the spacing sub * row_bytes: at some
 // spacings many windows land on the same ones and the kernels slow down by up
-// to 25% (measured on MI355X with every base alignment of the buffers tried:
-// the effect follows the spacing, not the addresses).  kWinRate holds the
-// backward kernel's measured rate for bf16 rows of H = 2048 (4 KiB rows of
-// dy and y, 12 KiB of in_proj and d_in) at one full round of windows, for
-// window lengths kWinLo .. kWinHi-1: (TB/s - 4.0) * 100, median of three
-// sweeps.  For that row geometry a launch takes, among the window lengths from
-// the shortest that fits one round to 1/span above it, the one with the best
-// measured rate.  A longer window leaves some CUs idle: the backward, bound by
-// HBM, hardly notices (at 40 of 64 windows per channel group it still runs at
-// 95% of the full round's rate) and searches 1/8 above; the forward loses
-// ~0.6% per idle window and searches 1/64 above.  Other row geometries take
-// the shortest window.
+// to 30% (measured on MI355X with every base alignment of the buffers tried:
+// the effect follows the spacing, not the addresses).  The tables below hold
+// the backward kernel's measured rate at one full round of windows, for
+// window lengths kWinLo .. kWinHi-1 and three row geometries (row_bytes is the
+// dy / y row; in_proj and d_in rows are three times as long): (TB/s - 3.0) *
+// 100, median of three sweeps.  For a measured geometry a launch takes, among
+// the window lengths from the shortest that fits one round to 1/span above
+// it, the one with the best rate.  A longer window leaves some CUs idle: the
+// backward, bound by HBM, hardly notices (at 40 of 64 windows per channel
+// group it still runs at 95% of the full round's rate) and searches 1/8
+// above; the forward loses ~0.6% per idle window and searches 1/64 above (its
+// conflicts fall at the same spacings).  Other geometries take the shortest
+// window; so do 8 KiB rows (H = 2048, fp32), where the table's picks gained
+// under 1% in the backward at T = 65536 and lost as much in the forward.
 constexpr int kWinLo = 64;
 constexpr int kWinHi = 1024;
-constexpr unsigned char kWinRate[kWinHi - kWinLo] = {
-     82, 100,  93,  86,  99,  93,  92,  96, 101,  97,  93,  85,  93,  98, 104, 100, 103,  95, 108, 103,
-    114, 104,   0, 115, 116, 117, 109, 114, 108, 102, 106,  55,  95, 102, 108, 101,  82, 108, 103, 109,
-    109, 115,  74, 108,  85,  89,  41, 111, 116, 108, 111, 113, 109,  96,  94,  77, 109, 103, 109, 102,
-    115,  76,  96,  23,  87,  15, 108,  91, 110, 105, 103,  91, 119, 121, 100,  91, 115,  97, 113, 115,
-    114, 104, 114, 115,  97,  99,  90,  67, 111,  20, 118,  67, 126, 101, 128, 125, 119, 133, 111, 136,
-    135,  89,  99, 121, 135, 118, 113, 126,  66, 120, 123, 117, 120, 124, 133, 130, 134, 134, 137, 124,
-    128, 126, 124, 109, 123, 125,  66, 110, 102,  12, 109, 117, 113,   0, 101, 107,  94, 105, 122, 128,
-    120, 121, 113, 120, 118,  92, 114,  89,  60, 101, 102,  63,  99,  92, 109, 107,  90, 106, 121, 109,
-    126, 116,  71, 112, 118,  78, 119, 123, 110, 112, 116, 108,  99, 115, 114, 119, 126, 121, 125, 118,
-    112, 127, 119, 111, 129, 122, 111, 116, 116, 111,  78, 105, 101, 104,  65, 111, 120, 120, 111, 123,
-    124, 118, 108, 125, 124, 121,  95, 105, 125, 135, 123,  96,  99, 114, 118, 116, 117, 119, 115, 119,
-    123, 108, 123, 126, 118, 125,  70, 120, 116, 100, 108,  68,  78,  76,  86,  75,  87,  34,  81, 105,
-    114, 116,  75, 120, 125, 122, 101, 118, 119, 119, 104, 118, 122, 122, 120, 124, 111, 132, 121, 124,
-    113, 116, 128, 124, 129, 120, 108, 134, 111, 121, 120, 128, 127, 121, 103,  92, 117, 115, 113, 115,
-     86, 112, 121, 129, 125, 127, 121, 132, 118, 115, 116, 119, 123, 122, 112, 117, 111, 123, 133, 124,
-    133, 124, 123, 117, 130, 123, 121, 126, 127, 123, 126, 122, 124, 118, 121, 114,  89,  78,  80,  95,
-     99,  79,  68,  14,  80, 112, 129, 125, 112,  81,  54, 119, 126, 127, 130, 130, 123, 112, 110, 128,
-    128, 129, 134, 137, 127, 127, 130, 123, 111, 122, 130, 120, 128, 119, 111, 124, 132, 124, 115, 103,
-    111, 127, 126, 124, 125, 121,  98, 113, 127, 124, 124, 122, 125, 129, 125, 125, 115, 124, 130, 126,
-    125, 112, 107, 121, 135, 126, 126,  92,  50,  98, 118, 145, 134, 118,  61,  79, 123, 125, 131, 126,
-    109,  94,  86, 119, 111, 120, 118, 106, 112,  94, 114, 128, 122, 130, 128, 121, 124, 129, 113,  96,
-    106, 112, 125, 120, 117, 132, 127, 130, 110, 120, 119, 115, 126, 127, 123, 126, 120, 128, 126, 128,
-    137, 132, 130, 123,  99, 118, 133, 134, 136, 133, 131, 122,  96, 120, 133, 135, 136, 131, 130, 128,
-    123, 128, 122, 105, 119, 120, 122, 126, 129, 121, 124, 110, 107, 123, 120, 102, 116, 119, 107, 128,
-    131, 133, 139, 134, 130, 124,  83, 102, 114, 117, 124, 133, 124, 130, 118,  99, 110, 123, 122, 127,
-    133, 130, 130, 132, 130, 113, 119, 126, 134, 133, 136, 135, 127, 122, 121, 101,  54,  96, 125, 123,
-    128, 132, 121, 116, 123, 100,  58,  66,  90,  74, 107, 111, 116, 119, 117, 114, 103,  97,  73,  72,
-    103, 101, 128, 134, 118, 131, 121,  78, 105, 115, 129, 128, 135, 130, 124, 121, 122, 126, 128, 131,
-    120, 127, 130, 124, 125, 126, 128, 130, 132, 123, 122, 113, 119, 132, 131, 132, 120, 128, 134, 130,
-    108, 103, 120, 122, 117, 129, 124, 120, 130, 133, 129, 124, 128, 126, 122, 127, 121, 130, 134, 126,
-    123, 125, 127, 127, 125, 129, 137, 134, 144, 141, 129, 123, 110,  51,  95, 124, 135, 131, 147, 139,
-    135, 139, 126,  95,  64,  97, 108, 129, 129, 136, 138, 137, 130, 127, 121, 125, 125, 127, 130, 128,
-    130, 122, 124, 119, 127, 125, 126, 129, 130, 126, 126, 115, 124, 133, 121, 120, 100, 130, 126, 133,
-    135, 128, 131, 134, 135, 129, 115, 108, 113, 128, 124, 133, 134, 136, 128, 126, 133, 126, 129, 127,
-    126, 132, 129, 133, 131, 124, 125, 125, 122,  89, 108, 120, 121, 132, 125, 117, 112,  92,  89,  87,
-     78,  89,  94, 110, 128, 118, 102,  96,  99,  53,  50,  80,  97, 125, 125, 134, 141, 136, 132, 127,
-    126, 118, 106,  80,  99, 128, 124, 129, 134, 134, 133, 130, 129, 126, 128, 127, 129, 117, 125, 122,
-    105, 116, 127, 131, 127, 126, 124, 131, 125, 128, 134, 131, 122, 115, 119, 129, 128, 126, 132, 131,
-    118, 112, 113, 123, 117,  89, 112, 129, 131, 128, 123, 133, 122, 125, 122, 122, 120, 119, 123, 126,
-    124, 129, 124, 108, 127, 130, 135, 134, 132, 128, 131, 135, 132, 133, 131, 122, 116, 122, 129, 129,
-    127, 129, 128, 126, 112, 118, 117, 114, 118, 130, 126, 125, 127, 131, 128, 126, 119, 122, 126, 121,
-    122, 107, 112, 123, 113, 111, 116, 121, 118, 113, 126, 130, 131, 130, 125, 132, 129, 120,  94,  88,
-     86, 104, 111, 131, 135, 135, 139, 138, 138, 134, 127, 118,  88,  69, 102, 119, 131, 130, 128, 135,
-    134, 132, 128, 131, 122, 114, 115,  92, 110, 122, 123, 119, 120, 125, 128, 129, 125, 118, 121, 121,
-    125, 120, 113, 117, 121, 126, 127, 127, 126, 126, 133, 135, 134, 129, 124, 129, 125, 131, 130, 117,
-    116, 115,  79,  68,  94, 110, 112, 125, 122, 121, 112, 113, 121, 128, 127, 123, 114, 124, 117, 106,
-    104,  96, 111, 110, 113, 109, 115, 116, 124, 120, 127, 122, 123, 128, 132, 123, 125, 120, 126, 128,
-    127, 129, 128, 130, 133, 133, 127, 127, 128, 132, 132, 125, 112, 115, 124, 134, 133, 131, 129, 128,
+// H = 1024, 2-byte elements: 2 KiB rows, 2 channel groups
+constexpr unsigned char kWinRate2K[kWinHi - kWinLo] = {
+    154, 181, 172, 173, 197, 177, 187, 186, 185, 180, 182, 177, 186, 180, 188, 186, 187, 183, 189, 203,
+    199, 193,  41, 202, 202, 199, 192, 196, 191, 191, 185, 183, 189, 192, 194, 186, 172, 194, 183, 194,
+    193, 197, 196, 198, 159, 162,  94, 203, 212, 203, 213, 212, 207, 176, 176, 152, 191, 194, 194, 184,
+    200, 174, 187, 158, 174, 144, 203, 181, 194, 173, 184, 193, 204, 207, 194, 156, 199, 189, 199, 198,
+    204, 180, 199, 200, 195, 197, 191, 198, 203, 148, 195, 165, 206, 187, 205, 196, 199, 214, 204, 214,
+    209, 182, 196, 194, 222, 216, 208, 224, 130, 215, 221, 207, 214, 203, 212, 209, 210, 213, 215, 205,
+    211, 209, 195, 189, 201, 207, 171, 197, 192, 163, 195, 209, 208, 134, 197, 182, 195, 174, 207, 211,
+    203, 208, 207, 205, 205, 154, 212, 171, 173, 202, 207, 188, 198, 164, 185, 175, 142, 175, 204, 204,
+    212, 202, 199, 199, 209, 204, 210, 209, 202, 207, 188, 195, 189, 193, 175, 191, 206, 191, 206, 210,
+    205, 209, 195, 190, 216, 212, 173, 207, 203, 200, 130, 197, 186, 204, 128, 205, 212, 209, 187, 208,
+    212, 207, 198, 205, 205, 208, 196, 187, 212, 219, 212, 189, 203, 200, 183, 198, 206, 200, 190, 197,
+    208, 197, 210, 209, 208, 214, 205, 215, 200, 185, 209, 198, 198, 176, 192, 195, 193, 111, 196, 209,
+    214, 199, 133, 200, 209, 206, 172, 212, 214, 213, 197, 210, 218, 219, 212, 202, 199, 220, 218, 221,
+    208, 193, 222, 207, 219, 209, 182, 230, 192, 200, 198, 217, 225, 215, 206, 181, 225, 233, 232, 227,
+    179, 213, 219, 232, 217, 222, 215, 222, 198, 188, 213, 200, 222, 207, 210, 191, 219, 200, 222, 219,
+    223, 221, 210, 192, 220, 206, 213, 212, 205, 205, 197, 211, 209, 216, 211, 191, 175, 184, 197, 202,
+    201, 183, 160,  82, 195, 205, 214, 210, 198, 153, 103, 181, 195, 194, 199, 203, 197, 184, 195, 208,
+    215, 215, 218, 218, 206, 197, 212, 216, 204, 215, 206, 214, 209, 189, 189, 211, 216, 211, 188, 175,
+    176, 208, 209, 213, 209, 205, 156, 187, 209, 202, 203, 203, 204, 215, 201, 210, 180, 199, 198, 193,
+    210, 202, 196, 209, 209, 205, 200, 187, 169, 191, 206, 216, 215, 206, 173, 173, 214, 212, 209, 211,
+    194, 195, 198, 209, 204, 189, 196, 185, 204, 196, 199, 214, 199, 211, 207, 189, 210, 208, 208, 205,
+    209, 214, 202, 203, 196, 215, 211, 216, 209, 196, 204, 208, 212, 212, 213, 207, 196, 204, 207, 214,
+    210, 205, 209, 193, 164, 186, 204, 204, 202, 204, 208, 197, 170, 197, 217, 217, 224, 219, 216, 212,
+    205, 211, 213, 207, 215, 205, 205, 210, 203, 204, 215, 208, 214, 211, 210, 172, 193, 197, 182, 201,
+    213, 214, 225, 215, 212, 213, 185, 181, 198, 175, 210, 216, 199, 208, 205, 200, 205, 201, 201, 200,
+    199, 198, 205, 206, 208, 203, 204, 209, 216, 211, 214, 220, 205, 207, 209, 192, 190, 196, 213, 212,
+    203, 208, 184, 203, 207, 178, 160, 178, 174, 149, 188, 167, 191, 191, 192, 186, 195, 172, 123, 127,
+    189, 200, 211, 220, 210, 209, 197, 134, 168, 197, 211, 209, 208, 206, 200, 188, 188, 191, 203, 202,
+    205, 201, 204, 196, 197, 197, 214, 212, 218, 207, 215, 197, 210, 216, 210, 212, 201, 213, 219, 218,
+    208, 196, 215, 196, 198, 212, 203, 190, 215, 216, 212, 214, 214, 202, 208, 209, 197, 199, 214, 202,
+    200, 216, 210, 202, 213, 213, 216, 206, 218, 212, 210, 207, 203, 147, 191, 207, 216, 210, 215, 213,
+    213, 214, 221, 204, 147, 203, 216, 217, 213, 220, 223, 210, 214, 206, 214, 198, 216, 214, 215, 207,
+    207, 213, 192, 185, 209, 210, 207, 209, 212, 210, 212, 200, 207, 209, 198, 208, 206, 213, 206, 216,
+    217, 210, 205, 213, 214, 207, 208, 197, 204, 206, 193, 204, 207, 207, 199, 204, 208, 208, 213, 213,
+    214, 213, 210, 204, 212, 208, 203, 210, 208, 185, 198, 198, 212, 203, 196, 192, 186, 177, 173, 163,
+    174, 192, 193, 195, 211, 188, 182, 176, 174, 119, 115, 155, 177, 207, 210, 213, 220, 219, 213, 206,
+    204, 190, 156, 135, 153, 186, 181, 200, 206, 200, 207, 211, 213, 211, 213, 210, 209, 196, 203, 199,
+    209, 205, 217, 215, 216, 220, 215, 217, 215, 211, 220, 214, 213, 204, 212, 214, 212, 203, 209, 210,
+    198, 195, 209, 215, 206, 186, 206, 214, 220, 204, 189, 211, 199, 205, 207, 212, 216, 211, 204, 201,
+    194, 196, 187, 165, 192, 201, 210, 204, 208, 208, 209, 213, 207, 212, 213, 190, 178, 196, 208, 212,
+    212, 214, 213, 202, 214, 211, 208, 213, 208, 214, 213, 211, 207, 216, 211, 201, 198, 188, 209, 208,
+    209, 206, 213, 214, 213, 204, 208, 188, 194, 197, 205, 214, 217, 208, 206, 206, 200, 200, 178, 151,
+    144, 181, 192, 203, 213, 218, 224, 225, 218, 215, 209, 185, 166, 144, 166, 181, 211, 208, 211, 212,
+    217, 215, 213, 216, 201, 182, 184, 155, 180, 202, 203, 209, 205, 202, 211, 209, 204, 199, 197, 197,
+    210, 200, 176, 194, 207, 208, 215, 210, 208, 206, 212, 211, 208, 195, 200, 209, 206, 205, 209, 209,
+    207, 202, 172, 175, 199, 217, 210, 209, 208, 207, 209, 201, 199, 215, 217, 214, 210, 217, 203, 193,
+    198, 176, 188, 205, 207, 205, 203, 188, 211, 220, 209, 200, 205, 216, 208, 206, 200, 193, 210, 213,
+    208, 214, 216, 212, 220, 215, 216, 212, 213, 214, 210, 199, 178, 193, 207, 214, 216, 215, 217, 216,
+};
+// H = 1536, 2-byte elements: 3 KiB rows, 3 channel groups
+constexpr unsigned char kWinRate3K[kWinHi - kWinLo] = {
+    183, 190, 177, 157, 170, 185, 190, 188, 157, 151, 192, 199, 212, 211, 150, 155, 180, 195, 179, 196,
+    182, 175, 128, 187, 187, 184, 190, 202, 182, 175, 181, 180, 200, 198, 195, 155, 179, 195, 116, 182,
+    207, 182, 202, 212, 195, 205, 185, 205, 232, 116, 206, 214, 226, 215, 212, 200, 211, 210, 202, 202,
+    196, 206, 205, 183, 194, 102, 194, 130, 192, 190, 186, 204, 194, 212, 197, 164, 217, 187, 206, 207,
+    187, 204, 169, 187, 207, 205, 203, 218, 218, 196, 214, 211, 191, 137, 190, 199, 204, 183, 212, 206,
+    195, 211, 207, 194, 203, 200, 188, 193, 106, 211, 209, 196, 214, 214, 204, 195, 191, 213, 222, 207,
+    189, 211, 211, 205, 201, 214, 207, 211, 214, 199, 219, 203, 208, 200, 154, 196, 190,  86, 212, 185,
+    105, 204, 198, 194, 214, 199, 204, 214, 220, 222, 227, 211, 206, 203, 214, 191, 183, 191, 223, 224,
+    246, 224, 193, 235, 247, 203, 220, 233, 230, 205, 215, 229, 224, 208, 201, 218, 225, 205, 223, 226,
+    214, 212, 213, 218, 216, 200, 215, 214, 218, 176, 184, 205, 199, 171,  83, 201, 221, 211, 133, 151,
+    202, 207, 203, 169, 197, 214, 224, 215, 214, 212, 219, 210, 211, 220, 187, 210, 219, 216, 170, 196,
+    209, 217, 198, 191, 209, 182, 210, 213, 196, 214, 197, 199, 220, 207, 218, 222, 209, 182, 211, 229,
+    224, 205, 188, 222, 218, 216, 195, 210, 213, 197, 185, 216, 205, 220, 212, 187, 218, 203, 196, 220,
+    209, 205, 220, 221, 214, 196, 208, 230, 212, 193, 209, 221, 222, 218, 222, 182, 216, 218, 212, 219,
+    172, 226, 217, 230, 219, 215, 209, 219, 217, 214, 220, 200, 220, 204, 211, 205, 192, 191, 208, 213,
+    235, 214, 215, 166, 189, 169, 219, 217, 209, 214, 212, 215, 211, 226, 222, 220, 211, 220, 220, 223,
+    208, 220, 195, 165, 217, 215, 211, 211, 211, 187, 163, 146, 161, 186, 196, 191, 201, 153, 107, 192,
+    221, 224, 217, 147, 162, 209, 222, 222, 219, 186, 210, 221, 218, 209, 200, 203, 217, 219, 209, 220,
+    216, 212, 223, 211, 228, 225, 206, 218, 197, 210, 202, 216, 218, 219, 206, 212, 186, 206, 210, 216,
+    216, 215, 219, 224, 232, 220, 226, 203, 177, 229, 222, 236, 231, 234, 203, 169, 208, 226, 228, 222,
+    220, 220, 212, 216, 220, 203, 211, 205, 220, 218, 210, 220, 210, 212, 220, 193, 204, 210, 218, 212,
+    209, 223, 221, 221, 218, 220, 221, 225, 209, 221, 218, 222, 218, 218, 208, 210, 209, 213, 178, 205,
+    220, 211, 194, 173, 157, 150, 184, 198, 206, 194, 170, 127, 111, 166, 204, 216, 228, 224, 221, 208,
+    162, 126, 190, 213, 219, 218, 225, 229, 224, 219, 199, 204, 206, 216, 221, 211, 219, 228, 220, 221,
+    218, 212, 222, 200, 215, 218, 198, 222, 214, 214, 227, 221, 201, 214, 208, 205, 227, 220, 208, 206,
+    191, 197, 221, 220, 217, 216, 224, 221, 211, 183, 198, 213, 220, 219, 209, 220, 212, 210, 219, 221,
+    214, 220, 208, 209, 213, 216, 214, 222, 220, 209, 189, 182, 218, 222, 222, 217, 218, 198, 155, 162,
+    206, 224, 230, 235, 231, 223, 199, 143, 158, 209, 212, 222, 226, 212, 221, 167, 172, 182, 190, 212,
+    203, 207, 209, 210, 195, 209, 203, 175, 205, 212, 214, 207, 221, 224, 213, 216, 221, 222, 222, 216,
+    164, 191, 220, 205, 216, 210, 202, 215, 223, 223, 221, 206, 212, 195, 197, 209, 205, 212, 231, 217,
+    211, 221, 211, 205, 217, 217, 223, 218, 228, 221, 223, 225, 222, 173, 196, 218, 227, 221, 226, 227,
+    226, 220, 228, 202, 182, 200, 223, 227, 224, 225, 220, 213, 223, 209, 224, 207, 222, 222, 202, 195,
+    209, 222, 201, 201, 223, 221, 212, 216, 194, 207, 195, 215, 221, 212, 200, 194, 214, 219, 197, 199,
+    221, 226, 223, 226, 233, 230, 221, 221, 219, 202, 170, 192, 213, 177, 195, 221, 223, 221, 216, 213,
+    210, 184, 202, 205, 214, 221, 217, 219, 221, 225, 225, 222, 220, 215, 208, 214, 205, 210, 219, 226,
+    222, 223, 222, 217, 219, 214, 212, 210, 196, 133, 162, 216, 211, 219, 221, 221, 220, 219, 222, 217,
+    213, 198, 186, 152, 159, 191, 166, 194, 193, 192, 199, 208, 215, 211, 215, 209, 206, 196, 184, 151,
+    155, 192, 208, 214, 220, 234, 228, 219, 223, 202, 196, 157, 199, 195, 215, 221, 220, 223, 226, 218,
+    215, 218, 210, 217, 213, 219, 226, 218, 218, 218, 211, 222, 215, 217, 216, 219, 219, 223, 224, 221,
+    215, 217, 204, 193, 206, 223, 221, 222, 221, 218, 218, 225, 225, 225, 215, 207, 188, 204, 214, 198,
+    201, 223, 221, 206, 211, 221, 219, 221, 218, 214, 219, 222, 215, 218, 215, 216, 214, 202, 216, 206,
+    216, 216, 214, 211, 217, 213, 219, 215, 218, 217, 228, 225, 229, 227, 223, 222, 202, 204, 189, 161,
+    192, 218, 225, 229, 228, 234, 238, 235, 232, 228, 226, 208, 185, 162, 156, 179, 208, 215, 222, 223,
+    228, 226, 223, 221, 216, 214, 216, 207, 212, 222, 218, 219, 218, 217, 214, 208, 213, 221, 217, 215,
+    216, 220, 220, 218, 223, 220, 223, 219, 217, 218, 214, 223, 222, 209, 200, 197, 192, 211, 218, 214,
+    223, 224, 216, 213, 217, 219, 227, 231, 219, 210, 202, 191, 196, 217, 215, 215, 222, 219, 222, 226,
+    221, 217, 220, 217, 215, 219, 210, 213, 220, 218, 223, 220, 217, 226, 214, 217, 207, 213, 209, 210,
+    184, 188, 204, 209, 222, 228, 226, 207, 213, 196, 202, 197, 181, 186, 166, 175, 184, 183, 207, 212,
+};
+// H = 2048, 2-byte elements: 4 KiB rows, 4 channel groups
+constexpr unsigned char kWinRate4K[kWinHi - kWinLo] = {
+    182, 200, 193, 186, 199, 193, 192, 196, 201, 197, 193, 185, 193, 198, 204, 200, 203, 195, 208, 203,
+    214, 204,  82, 215, 216, 217, 209, 214, 208, 202, 206, 155, 195, 202, 208, 201, 182, 208, 203, 209,
+    209, 215, 174, 208, 185, 189, 141, 211, 216, 208, 211, 213, 209, 196, 194, 177, 209, 203, 209, 202,
+    215, 176, 196, 123, 187, 115, 208, 191, 210, 205, 203, 191, 219, 221, 200, 191, 215, 197, 213, 215,
+    214, 204, 214, 215, 197, 199, 190, 167, 211, 120, 218, 167, 226, 201, 228, 224, 219, 233, 211, 236,
+    235, 189, 199, 221, 235, 218, 213, 226, 166, 220, 223, 217, 220, 224, 233, 230, 234, 234, 237, 224,
+    228, 226, 224, 209, 223, 226, 166, 210, 202, 112, 209, 217, 213,  90, 201, 207, 194, 205, 222, 228,
+    220, 221, 213, 220, 218, 192, 214, 189, 160, 201, 202, 163, 199, 192, 209, 207, 190, 206, 221, 209,
+    226, 216, 171, 212, 218, 178, 219, 223, 210, 212, 216, 208, 199, 215, 214, 219, 226, 221, 225, 218,
+    212, 227, 219, 211, 229, 222, 211, 216, 216, 211, 178, 205, 201, 204, 165, 211, 220, 220, 211, 223,
+    224, 218, 208, 225, 224, 221, 195, 205, 225, 235, 223, 196, 199, 214, 218, 216, 217, 219, 215, 219,
+    223, 208, 223, 226, 218, 225, 170, 220, 216, 200, 208, 168, 178, 176, 186, 174, 187, 134, 181, 205,
+    214, 216, 175, 220, 226, 222, 201, 218, 219, 219, 204, 218, 222, 222, 220, 224, 211, 232, 221, 224,
+    213, 216, 228, 224, 229, 220, 208, 234, 211, 221, 220, 228, 227, 221, 203, 192, 217, 215, 213, 215,
+    186, 212, 221, 229, 225, 227, 221, 232, 218, 215, 216, 219, 223, 222, 212, 217, 211, 223, 233, 224,
+    233, 224, 223, 217, 230, 223, 222, 226, 227, 223, 226, 222, 224, 218, 221, 214, 189, 178, 180, 195,
+    199, 179, 168, 114, 180, 212, 229, 225, 212, 181, 154, 219, 226, 227, 230, 230, 223, 212, 210, 228,
+    228, 229, 234, 237, 227, 227, 230, 223, 211, 222, 230, 220, 228, 219, 211, 224, 232, 224, 215, 203,
+    211, 227, 226, 224, 225, 221, 198, 213, 227, 224, 224, 222, 226, 229, 225, 224, 215, 224, 230, 226,
+    225, 212, 207, 221, 235, 226, 226, 192, 150, 198, 218, 245, 234, 218, 161, 179, 223, 224, 231, 226,
+    209, 194, 186, 219, 211, 220, 218, 206, 212, 194, 214, 228, 222, 230, 228, 221, 224, 229, 213, 196,
+    206, 212, 225, 220, 217, 232, 227, 230, 210, 220, 219, 215, 226, 227, 223, 226, 220, 228, 226, 228,
+    237, 232, 230, 223, 199, 218, 233, 234, 236, 233, 231, 222, 196, 220, 233, 235, 236, 231, 230, 228,
+    223, 228, 222, 205, 219, 220, 222, 226, 229, 221, 224, 210, 207, 223, 220, 202, 216, 219, 207, 228,
+    231, 233, 239, 234, 230, 224, 183, 202, 214, 217, 224, 233, 224, 230, 218, 199, 210, 223, 222, 227,
+    233, 230, 230, 232, 230, 213, 219, 226, 234, 233, 236, 235, 227, 222, 221, 201, 154, 196, 225, 223,
+    228, 232, 221, 216, 223, 200, 158, 166, 190, 174, 207, 211, 216, 219, 217, 214, 203, 197, 173, 172,
+    203, 201, 228, 234, 218, 231, 221, 178, 205, 215, 229, 228, 235, 230, 224, 221, 222, 226, 228, 231,
+    220, 227, 230, 224, 226, 226, 228, 230, 232, 223, 222, 213, 219, 232, 231, 232, 220, 228, 234, 230,
+    208, 203, 220, 222, 217, 229, 224, 220, 230, 233, 229, 224, 228, 226, 222, 227, 221, 230, 234, 226,
+    223, 225, 227, 227, 225, 229, 237, 234, 244, 241, 229, 223, 210, 151, 195, 224, 235, 231, 247, 239,
+    235, 239, 226, 195, 164, 197, 208, 229, 229, 236, 238, 237, 230, 227, 221, 225, 225, 227, 230, 228,
+    230, 222, 224, 219, 227, 225, 226, 229, 230, 226, 226, 215, 224, 233, 221, 220, 200, 230, 226, 233,
+    235, 228, 231, 234, 235, 229, 215, 208, 213, 228, 224, 233, 234, 236, 228, 226, 233, 226, 229, 227,
+    226, 232, 229, 233, 231, 224, 225, 225, 222, 189, 208, 220, 222, 232, 225, 217, 212, 192, 189, 187,
+    178, 189, 194, 210, 228, 218, 202, 196, 199, 153, 150, 180, 197, 225, 224, 234, 241, 236, 232, 227,
+    226, 218, 206, 180, 199, 228, 224, 229, 234, 234, 233, 230, 229, 226, 228, 227, 229, 217, 225, 222,
+    205, 216, 227, 231, 227, 226, 224, 231, 225, 228, 234, 231, 222, 215, 219, 229, 228, 226, 232, 231,
+    218, 212, 213, 223, 217, 189, 212, 229, 231, 228, 223, 233, 222, 225, 222, 222, 220, 219, 223, 226,
+    224, 229, 224, 208, 227, 230, 235, 234, 232, 228, 231, 235, 232, 233, 231, 222, 216, 222, 229, 229,
+    227, 229, 228, 226, 212, 218, 217, 214, 218, 230, 226, 225, 227, 231, 228, 226, 219, 222, 226, 221,
+    222, 207, 212, 223, 213, 211, 216, 221, 218, 213, 226, 230, 231, 230, 225, 232, 229, 220, 194, 188,
+    186, 204, 211, 231, 235, 235, 239, 238, 238, 234, 227, 218, 188, 169, 202, 219, 231, 230, 228, 235,
+    234, 232, 228, 231, 222, 214, 215, 192, 210, 222, 223, 219, 220, 225, 228, 229, 225, 218, 221, 221,
+    225, 220, 213, 217, 221, 226, 227, 227, 226, 226, 233, 235, 234, 229, 224, 229, 225, 231, 230, 217,
+    216, 215, 179, 168, 194, 210, 212, 225, 222, 221, 212, 213, 222, 228, 227, 223, 214, 224, 217, 206,
+    204, 196, 211, 210, 213, 209, 215, 216, 224, 220, 227, 222, 223, 228, 232, 223, 225, 220, 226, 228,
+    227, 229, 228, 230, 233, 233, 227, 227, 228, 232, 232, 225, 212, 215, 224, 234, 233, 231, 229, 228,
 };
 
 constexpr int kWinSpanBwd = 8;
 constexpr int kWinSpanFwd = 64;
 
-inline int64_t pick_window(int64_t sub0, int64_t row_bytes, int span) {
-    if (row_bytes != 4096 || sub0 < kWinLo || sub0 >= kWinHi || span < 1) return sub0;
+// The measured table for rows of row_bytes split into `groups` channel groups,
+// or nullptr.
+inline const unsigned char* win_rate_table(int64_t row_bytes, int groups) {
+    if (row_bytes == 2048 && groups == 2) return kWinRate2K;
+    if (row_bytes == 3072 && groups == 3) return kWinRate3K;
+    if (row_bytes == 4096 && groups == 4) return kWinRate4K;
+    return nullptr;
+}
+
+inline int64_t pick_window(int64_t sub0, int64_t row_bytes, int groups, int span) {
+    const unsigned char* rate = LFM2SC_WIN_TABLES ? win_rate_table(row_bytes, groups) : nullptr;
+    if (rate == nullptr || sub0 < kWinLo || sub0 >= kWinHi || span < 1) return sub0;
     const int64_t last = sub0 + (sub0 + span - 1) / span;
     int64_t best = sub0;
     for (int64_t s = sub0 + 1; s <= last && s < kWinHi; ++s)
-        if (kWinRate[s - kWinLo] > kWinRate[best - kWinLo]) best = s;
+        if (rate[s - kWinLo] > rate[best - kWinLo]) best = s;
     return best;
 }
 
@@ -459,7 +577,7 @@ inline Tiling ragged_tiling(int64_t total_T, int N, int groups, int resident, in
     int64_t sub = (total_T + denom - 1) / denom;
     if (sub < LFM2SC_SUB_MIN) sub = LFM2SC_SUB_MIN;
     if (sub > (1 << 24)) sub = 1 << 24;
-    sub = pick_window(sub, row_bytes, span);
+    sub = pick_window(sub, row_bytes, groups, span);
 
     const int64_t gap = sub * tw;
     return Tiling{(int)sub, (total_T + gap - 1) / gap + gaps};
