@@ -179,6 +179,27 @@ def test_workspace_bytes(L):
     assert f(9, 2048, 3, 64, 1) == 0 and f(0, 12, 3, 64, 1) == 0 and f(0, 2048, 5, 64, 1) == 0
 
 
+def test_window_tables_pick_measured_lengths(L):
+    """The backward's window length at T=65536, one sequence, seen through its workspace (one partial row of
+    H x (K+1) sums per window of 4 waves).  Row geometries with a measured rate table take the best-rated
+    length up to 1/8 above the shortest one-round length; the others keep the shortest."""
+    f = L.lfm2sc_backward_workspace_bytes
+    T = 65536
+
+    def windows(sub):
+        return -(-T // (4 * sub))
+
+    # (dtype, H, window length picked, accumulator bytes): 2 KiB, 3 KiB and 4 KiB bf16 rows have tables
+    cases = [(0, 1024, 137, 4), (0, 1536, 228, 4), (0, 2048, 273, 4),
+             (1, 2048, 256, 8),   # 8 KiB fp32 rows: no table
+             (1, 1024, 128, 8),   # 4 KiB rows in 2 channel groups: the 4 KiB table is for 4 groups only
+             (0, 512, 64, 4)]     # 1 KiB rows: no table
+    for dtype, H, sub, acc in cases:
+        got = f(dtype, H, 3, T, 1)
+        want = windows(sub) * H * 4 * acc
+        assert got == (want + 255) // 256 * 256, (dtype, H, got, want)
+
+
 def test_binding_names_match_c_abi():
     import gated_short_causal_amd as g
     for n in ("lfm2sc_prefill_ragged", "lfm2sc_decode_step", "lfm2sc_verify_window", "lfm2sc_commit_window",
