@@ -229,6 +229,46 @@ def copy_ceiling(reps=10):
             "kernel": "torch copy_ of 1 GiB, device to device", "reps": reps}
 
 
+def mix_reference(reps=10):
+    """The runtime's own elementwise kernels at several shares of written bytes (torch fill_, copy_, add,
+    addcmul over 1 GiB-scale buffers), GB/s read + written, median of `reps`: how fast this box streams a
+    plain read/write mix, beside which the ShortConv kernels' own shares (forward 1/4, decode 2/5, backward
+    3/7 of their bytes written) can be read.  Context, not a ceiling."""
+    import statistics
+    import torch
+
+    def med(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return statistics.median(ts)
+
+    n = 1 << 28   # bf16 elements per operand (512 MiB)
+    x = torch.randn(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn_like(x)
+    z = torch.randn_like(x)
+    o = torch.empty_like(x)
+    e = 2 * n
+    out = {}
+    for name, w, nbytes, fn in (("fill_", 1.0, e, lambda: o.fill_(1.0)),
+                                ("copy_", 0.5, 2 * e, lambda: o.copy_(x)),
+                                ("add", 1 / 3, 3 * e, lambda: torch.add(x, y, out=o)),
+                                ("addcmul", 0.25, 4 * e, lambda: torch.addcmul(x, y, z, out=o))):
+        ms = med(fn)
+        out[name] = {"written_share": round(w, 3), "GB/s": round(nbytes / ms / 1e6, 1)}
+    del x, y, z, o
+    torch.cuda.empty_cache()
+    return out
+
+
 def timed_loop(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -604,6 +644,7 @@ def main():
     cc["step_frac"] = round(value / cc["GB/s"], 4)
     cc["backward_frac"] = round(bwd_gbs / cc["GB/s"], 4)
     line["copy_ceiling"] = cc
+    line["mix_reference"] = mix_reference()
     if args.extra:
         line["extra"] = extra_measurements(wl, max(2, args.steps // 2), args.fused)
     if not args.no_cpu:
