@@ -145,6 +145,10 @@ RAGGED_INT = [
     ([1, 2, 3, 1000, 4097, 0, 5, 777, 10001, 64, 2, 3333], 2048, 3),
     ([7, 2049, 1, 300, 5000, 2], 1032, 4),
     ([2, 9, 4099, 1, 643], 520, 2),
+    # window lengths from the measured rate tables of 3 KiB and 2 KiB rows (one round of windows of ~132 and
+    # ~81 tokens, then the table's pick a few tokens longer), with sequence gaps on the virtual axis
+    ([9000, 13, 17000, 3, 14000], 1536, 3),
+    ([25000, 5, 15000, 1], 1024, 3),
 ]
 
 
