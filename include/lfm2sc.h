@@ -22,7 +22,9 @@
  *    synchronisation.
  *  - dtype: LFM2SC_BF16 or LFM2SC_F32.  It applies to the in_proj rows, the
  *    weight, the state pool, y, the tape, dy and d_in alike.  Arithmetic is
- *    fp32 in registers; each output element is rounded once (RNE) when stored.
+ *    fp32 in registers (fp64 in the backward with fp32 I/O, where products of
+ *    two fp32 values are exact); each output element is rounded once (RNE)
+ *    when stored.
  *    In bf16 mode B*xv and dy*C are exact in fp32, so every stored state or
  *    tape entry equals the exact value rounded to bf16.
  *  - Layouts are row-major; every "stride" is in ELEMENTS between consecutive
