@@ -251,17 +251,23 @@ __device__ __forceinline__ rsrc_t row_rsrc(const void* row, uint32_t row_bytes) 
 }
 
 // Cache-policy operands of the buffer loads and stores (gfx950: bit 0 sc0,
-// bit 1 nt, bit 4 sc1).  Streamed loads take nt.  Stores all take sc1
+// bit 1 nt, bit 4 sc1).  Streamed loads take nt.  bf16 stores take sc1
 // (system scope, i.e. written through), with nt where the NT knob asks for
 // it.  Measured on MI355X (median of 3-4 runs each): the backward's d_in
 // stores as nt sc1 take the T=65536 step from 533.8 to 530.3 us (nt alone is
 // the former; sc1 alone 577 us); then the forward's y stores as sc1 take it to
 // 525.8 us (forward 175.1 -> 168.5 us; nt sc1 196 us, sc0 sc1 the same as
 // sc1), the T=4096 step from 43.9 to 42.5 us and the ragged prefill from 28.3
-// to 27.8 us.
-constexpr int kPolicyStreamLoad = 2;
-constexpr int kPolicyStore = 16;
-constexpr int kPolicyStreamStore = 2 | 16;
+// to 27.8 us.  Written through, a store must cover whole cache lines: with
+// fp32 I/O a lane holds two 16-byte chunks, so each store instruction of a
+// wave covers every other 16 bytes of its 2 KiB, and sc1 made the fp32 step
+// 2x slower (1.24 -> 2.55 ms at H=2048).  fp32 stores keep nt only.
+constexpr int kPolicyNt = 2;
+constexpr int kPolicySc1 = 16;
+template <typename E>
+constexpr int store_policy(bool nt) {
+    return (nt ? kPolicyNt : 0) | (Elem<E>::kChunks == 1 ? kPolicySc1 : 0);
+}
 
 template <typename E, int NT>
 __device__ __forceinline__ Raw8<E> bld8(rsrc_t r, uint32_t voff) {
@@ -269,7 +275,7 @@ __device__ __forceinline__ Raw8<E> bld8(rsrc_t r, uint32_t voff) {
 #pragma unroll
     for (int i = 0; i < Elem<E>::kChunks; ++i) {
         const u32x4 v =
-            __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u * i, 0, (NT & 1) ? kPolicyStreamLoad : 0);
+            __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16u * i, 0, (NT & 1) ? kPolicyNt : 0);
         out.c[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
     return out;
@@ -280,7 +286,7 @@ __device__ __forceinline__ void bst8(rsrc_t r, uint32_t voff, const Raw8<E>& v) 
 #pragma unroll
     for (int i = 0; i < Elem<E>::kChunks; ++i) {
         const u32x4 w = {v.c[i].x, v.c[i].y, v.c[i].z, v.c[i].w};
-        __builtin_amdgcn_raw_buffer_store_b128(w, r, voff + 16u * i, 0, (NT & 2) ? kPolicyStreamStore : kPolicyStore);
+        __builtin_amdgcn_raw_buffer_store_b128(w, r, voff + 16u * i, 0, store_policy<E>((NT & 2) != 0));
     }
 }
 
