@@ -57,6 +57,10 @@
 #ifndef LFM2SC_DEC_NT
 #define LFM2SC_DEC_NT 3        // non-temporal hints in decode (bits): 1 in_proj loads, 2 y stores, 4 state loads,
 #endif                         // 8 state stores.  Measured at N=4096: 0 -> 38.6 us, 3 -> 32.2, 7 -> 40.2, 15 -> 50.1
+#ifndef LFM2SC_DEC_STAGE_N
+#define LFM2SC_DEC_STAGE_N 512   // decode calls of at least this many sequences stage the slot states through LDS.
+#endif                           // Per call by graph replay, lane-owned / staged: N=256 4.14 / 4.17 us, 512 6.01 /
+                                 // 5.78, 1024 10.2 / 9.3, 2048 17.9 / 16.0, 4096 32.4 / 29.9
 #ifndef LFM2SC_VER_NT
 #define LFM2SC_VER_NT 11       // same for verify: 1 in_proj loads, 2 y stores, 4 state loads, 8 tape stores.
 #endif                         // Measured at 64 x 8: 0 -> 6.24 us, 2 -> 6.10, 10 -> 5.95, 11 -> 5.89

@@ -168,6 +168,36 @@ def test_out_of_range_slots_are_skipped():
     assert_bits(g.pool, expect, "pool: only valid slots written")
 
 
+@pytest.mark.parametrize("K,dtype,H", [(1, torch.bfloat16, 2048), (2, torch.float32, 520), (3, torch.bfloat16, 520),
+                                         (4, torch.bfloat16, 1024), (4, torch.float32, 24), (3, torch.float32, 2048)])
+def test_decode_batches_staging_states(K, dtype, H):
+    """Batches large enough that decode stages each wave's state block through LDS (600 sequences): every K,
+    both dtypes, a channel count that leaves a partial wave group, some slot ids out of range (zero state,
+    nothing written), and a conv bias.  y against the oracle, the pool bit for bit."""
+    _say(f"case: staged decode K={K} {dtype} H={H} N=600")
+    N, slots = 600, 700
+    c = wl.decode_lfm2(seed=90 + K + H, N=N, slots=slots, H=H, K=K, dtype=dtype)
+    slot_idx = c.slot_idx.clone()
+    slot_idx[5] = slots          # past the pool
+    slot_idx[77] = -3            # negative
+    bias = (torch.rand(H, generator=torch.Generator().manual_seed(K)) - 0.5).to(dtype)
+    g = c.to(DEV)
+    pool0 = g.pool.clone()
+    y = _nan((N, H), dtype)
+    lfm2sc_decode_step(g.inp, g.w, g.pool, slot_idx.to(DEV), y, bias=bias.to(DEV))
+    torch.cuda.synchronize()
+    ok = [i for i in range(N) if 0 <= int(slot_idx[i]) < slots]
+    bad = [5, 77]
+    y_ok, p_ok = oracle.decode(c.inp[ok], c.w, c.pool, slot_idx[ok], bias=bias)
+    y_bad, _ = oracle.decode(c.inp[bad], c.w, np.zeros((2, H, K)), [0, 1], bias=bias)
+    assert_close(y[ok], y_ok, dtype, "y, valid slots")
+    assert_close(y[bad], y_bad, dtype, "y, skipped slots use a zero state")
+    expect = pool0.cpu().clone()
+    used = slot_idx[ok].long()
+    expect[used] = rounded(p_ok[used.numpy()], dtype)
+    assert_bits(g.pool, expect, "pool: valid slots advanced, every other slot untouched")
+
+
 def test_graph_capture_replays_match_eager():
     """Prefill + backward + decode captured in one HIP graph; each replay (with eager work and syncs in
     between) must reproduce the eager results bitwise."""
