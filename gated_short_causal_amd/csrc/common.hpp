@@ -61,6 +61,12 @@
 #define LFM2SC_DEC_STAGE_N 512   // decode calls of at least this many sequences stage the slot states through LDS.
 #endif                           // Per call by graph replay, lane-owned / staged: N=256 4.14 / 4.17 us, 512 6.01 /
                                  // 5.78, 1024 10.2 / 9.3, 2048 17.9 / 16.0, 4096 32.4 / 29.9
+#ifndef LFM2SC_VER_STAGE
+#define LFM2SC_VER_STAGE 1       // 1: verify writes each step's tape row through LDS, 1 KiB per store instruction
+#endif                           // (64 x 8 draft tokens: 5.89 us per call with one lane per block, 4.55 staged)
+#ifndef LFM2SC_CVU_STAGE
+#define LFM2SC_CVU_STAGE 1       // 1: the tape-mode conv update writes its tape blocks through LDS, as verify
+#endif                           // (64 x 8 on the transposed view: 5.85 us per call lane-owned, 4.99 staged)
 #ifndef LFM2SC_VER_NT
 #define LFM2SC_VER_NT 11       // same for verify: 1 in_proj loads, 2 y stores, 4 state loads, 8 tape stores.
 #endif                         // Measured at 64 x 8: 0 -> 6.24 us, 2 -> 6.10, 10 -> 5.95, 11 -> 5.89
@@ -296,6 +302,71 @@ __device__ __forceinline__ void bst8(rsrc_t r, uint32_t voff, const Raw8<E>& v) 
 
 template <typename E, int NT>
 __device__ __forceinline__ void bst8f(rsrc_t r, uint32_t voff, const float* f) { bst8<E, NT>(r, voff, from_f32<E>(f)); }
+
+// A wave's slot-state block (its 512 channels x K, contiguous in the slot)
+// moved between memory and the lanes through LDS.  A lane owns 8 channels x K
+// taps, 16*K contiguous bytes (bf16), so when each lane loads its own block
+// one load instruction of the wave touches every cache line of the wave's
+// block at a 16*K-byte stride, and the K instructions each touch them all.
+// Staged, instruction j moves the contiguous 1 KiB j of the block, and the
+// lanes exchange their pieces through LDS.  For decode batches this cut the
+// call at N=4096 from 32.4 to 29.9 us; it costs two barriers and an LDS round
+// trip, which small batches (N=256: 4.14 vs 4.17 us) do not earn back.
+template <typename E, int K>
+struct StateStage {
+    static constexpr int kCpl = K * Elem<E>::kChunks;   // 16-byte chunks per lane
+    uint4 buf[kCpl * kWave];
+};
+
+template <typename E, int K>
+__device__ __forceinline__ void stage_load(StateStage<E, K>& st, rsrc_t blk, int lane, float (&s)[kChPerLane][K]) {
+    constexpr int C = StateStage<E, K>::kCpl;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(blk, (uint32_t)(j * kWave + lane) * 16u, 0, 0);
+        st.buf[j * kWave + lane] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    __syncthreads();
+    float f[8 * K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        Raw8<E> r;
+#pragma unroll
+        for (int q = 0; q < Elem<E>::kChunks; ++q) r.c[q] = st.buf[lane * C + j * Elem<E>::kChunks + q];
+        to_f32(r, f + 8 * j);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) s[c][k] = f[c * K + k];
+}
+
+template <typename E, int K, int POLICY = 0>
+__device__ __forceinline__ void stage_store(StateStage<E, K>& st, rsrc_t blk, int lane,
+                                            const float (&s)[kChPerLane][K]) {
+    constexpr int C = StateStage<E, K>::kCpl;
+    float f[8 * K];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < K; ++k) f[c * K + k] = s[c][k];
+    __syncthreads();   // every lane has read its chunks of the load stage
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const Raw8<E> r = from_f32<E>(f + 8 * j);
+#pragma unroll
+        for (int q = 0; q < Elem<E>::kChunks; ++q) st.buf[lane * C + j * Elem<E>::kChunks + q] = r.c[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        const uint4 v = st.buf[j * kWave + lane];
+        const u32x4 w = {v.x, v.y, v.z, v.w};
+        __builtin_amdgcn_raw_buffer_store_b128(w, blk, (uint32_t)(j * kWave + lane) * 16u, 0, POLICY);
+    }
+    __syncthreads();   // the buffer is free for the next item
+}
+
 
 // ---------------------------------------------------------------- XCD-aware block order
 // MI355X dispatches consecutive workgroups round-robin over its 8 XCDs, each

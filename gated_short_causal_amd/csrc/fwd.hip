@@ -230,70 +230,6 @@ inline int small_groups(int64_t lanes) { return (int)((lanes + kSmallBlock - 1) 
 // One token per sequence, a lane = 8 channels.  Every load of a lane is
 // independent of the others except the state, whose address needs the
 // (wave-uniform, scalar-loaded) slot index.
-// A wave's slot-state block (its 512 channels x K, contiguous in the slot)
-// moved between memory and the lanes through LDS.  A lane owns 8 channels x K
-// taps, 16*K contiguous bytes (bf16), so when each lane loads its own block
-// one load instruction of the wave touches every cache line of the wave's
-// block at a 16*K-byte stride, and the K instructions each touch them all.
-// Staged, instruction j moves the contiguous 1 KiB j of the block, and the
-// lanes exchange their pieces through LDS.  For decode batches this cut the
-// call at N=4096 from 32.4 to 29.9 us; it costs two barriers and an LDS round
-// trip, which small batches (N=256: 4.14 vs 4.17 us) do not earn back.
-template <typename E, int K>
-struct StateStage {
-    static constexpr int kCpl = K * Elem<E>::kChunks;   // 16-byte chunks per lane
-    uint4 buf[kCpl * kSmallBlock];
-};
-
-template <typename E, int K>
-__device__ __forceinline__ void stage_load(StateStage<E, K>& st, rsrc_t blk, int lane, float (&s)[kChPerLane][K]) {
-    constexpr int C = StateStage<E, K>::kCpl;
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(blk, (uint32_t)(j * kSmallBlock + lane) * 16u, 0, 0);
-        st.buf[j * kSmallBlock + lane] = make_uint4(v.x, v.y, v.z, v.w);
-    }
-    __syncthreads();
-    float f[8 * K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-        Raw8<E> r;
-#pragma unroll
-        for (int q = 0; q < Elem<E>::kChunks; ++q) r.c[q] = st.buf[lane * C + j * Elem<E>::kChunks + q];
-        to_f32(r, f + 8 * j);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int k = 0; k < K; ++k) s[c][k] = f[c * K + k];
-}
-
-template <typename E, int K>
-__device__ __forceinline__ void stage_store(StateStage<E, K>& st, rsrc_t blk, int lane,
-                                            const float (&s)[kChPerLane][K]) {
-    constexpr int C = StateStage<E, K>::kCpl;
-    float f[8 * K];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int k = 0; k < K; ++k) f[c * K + k] = s[c][k];
-    __syncthreads();   // every lane has read its chunks of the load stage
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-        const Raw8<E> r = from_f32<E>(f + 8 * j);
-#pragma unroll
-        for (int q = 0; q < Elem<E>::kChunks; ++q) st.buf[lane * C + j * Elem<E>::kChunks + q] = r.c[q];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const uint4 v = st.buf[j * kSmallBlock + lane];
-        const u32x4 w = {v.x, v.y, v.z, v.w};
-        __builtin_amdgcn_raw_buffer_store_b128(w, blk, (uint32_t)(j * kSmallBlock + lane) * 16u, 0, 0);
-    }
-    __syncthreads();   // the buffer is free for the next item
-}
-
 // Decode with the state block staged through LDS (StateStage).
 template <typename E, int K>
 __device__ __forceinline__ void decode_one_staged(const DecodeArgs<E>& a, int i, int g) {
@@ -395,14 +331,18 @@ __global__ __launch_bounds__(kSmallBlock) void decode_kernel(const DecodeArgs<E>
 // xv rows.  Only blocks that start inside the first K-1 steps read the slot,
 // so most waves skip the slot -> state round trip, and more waves share the
 // work of one sequence.
-template <typename E, int K, int U>
+template <typename E, int K, int U, bool STAGED>
 __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g, int z) {
     constexpr int KH = K > 1 ? K - 1 : 1;
-    const int ch0 = (g * kSmallBlock + threadIdx.x) * kChPerLane;
-    if (ch0 >= a.H) return;
+    const int lane = (int)threadIdx.x;
+    const int chw = g * kSmallBlock * kChPerLane;   // the wave's first channel
+    int ch0 = chw + lane * kChPerLane;
+    const bool on = ch0 < a.H;
+    if (!STAGED && !on) return;
+    if (!on) ch0 = chw;   // staged: lanes past H work on a valid address and store nothing
     const int s0 = z * U;
     const int n = a.L - s0 < U ? a.L - s0 : U;
-    if (n <= 0) return;
+    if (n <= 0) return;   // wave-uniform
     const int H = a.H;
     const int64_t HK = (int64_t)H * K;
     const E* base = a.in + (int64_t)i * a.L * a.in_stride + ch0;
@@ -483,18 +423,27 @@ __device__ __forceinline__ void verify_one(const VerifyArgs<E>& a, int i, int g,
                 for (int k = 0; k < K - 1; ++k) conv = fmaf(wf[c][k], s[c][k], conv);
                 yv[c] = c8[c] * conv;
             }
-            store_f32x8s<E, LFM2SC_VER_NT>(ybase + (int64_t)(s0 + u) * a.y_stride, yv);
-            store_block_s<E, K, (LFM2SC_VER_NT & 8) ? 2 : 0>(tbase + (int64_t)(s0 + u) * HK, s);
+            if (on) store_f32x8s<E, LFM2SC_VER_NT>(ybase + (int64_t)(s0 + u) * a.y_stride, yv);
+            if constexpr (STAGED) {
+                // the tape row of this step through LDS: contiguous 1 KiB per store instruction
+                __shared__ StateStage<E, K> stage;
+                const int nch = H - chw < kSmallBlock * kChPerLane ? H - chw : kSmallBlock * kChPerLane;
+                const rsrc_t blk = row_rsrc(a.win + ((int64_t)i * a.L + s0 + u) * HK + (int64_t)chw * K,
+                                            (uint32_t)nch * K * (uint32_t)sizeof(E));
+                stage_store<E, K, (LFM2SC_VER_NT & 8) ? kPolicyNt : 0>(stage, blk, lane, s);
+            } else {
+                store_block_s<E, K, (LFM2SC_VER_NT & 8) ? 2 : 0>(tbase + (int64_t)(s0 + u) * HK, s);
+            }
         }
     }
 }
 
-template <typename E, int K, int U>
+template <typename E, int K, int U, bool STAGED>
 __global__ __launch_bounds__(kSmallBlock) void verify_kernel(const VerifyArgs<E> a, int groups, int nz) {
     const int64_t items = (int64_t)a.N * nz * groups;
     for (int64_t b = blockIdx.x; b < items; b += gridDim.x) {
         const SmallIdx ix = small_idx_seq_fastest(b, a.N, groups);
-        verify_one<E, K, U>(a, ix.i, ix.g, ix.z);
+        verify_one<E, K, U, STAGED>(a, ix.i, ix.g, ix.z);
     }
 }
 
@@ -582,8 +531,8 @@ static hipError_t verify_k(const VerifyArgs<E>& a, hipStream_t s) {
     constexpr int U = LFM2SC_VERIFY_U;
     const int groups = small_groups(a.H / kChPerLane);
     const int nz = (a.L + U - 1) / U;
-    hipLaunchKernelGGL((verify_kernel<E, K, U>), dim3(small_grid((int64_t)a.N * nz * groups)), dim3(kSmallBlock), 0,
-                       s, a, groups, nz);
+    hipLaunchKernelGGL((verify_kernel<E, K, U, LFM2SC_VER_STAGE != 0>), dim3(small_grid((int64_t)a.N * nz * groups)),
+                       dim3(kSmallBlock), 0, s, a, groups, nz);
     return hipGetLastError();
 }
 

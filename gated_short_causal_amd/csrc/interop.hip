@@ -113,8 +113,12 @@ template <typename E, int K, bool VEC>
 __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const ConvUpdateArgs<E> a) {
     constexpr int KH = K > 1 ? K - 1 : 1;
     const int i = blockIdx.x;
-    const int ch0 = (blockIdx.y * kSmallBlock + threadIdx.x) * kChPerLane;
-    if (ch0 >= a.H) return;
+    const int lane = (int)threadIdx.x;
+    const int chw = blockIdx.y * kSmallBlock * kChPerLane;   // the wave's first channel
+    int ch0 = chw + lane * kChPerLane;
+    const bool on = ch0 < a.H;
+    if (!LFM2SC_CVU_STAGE && !on) return;
+    if (!on) ch0 = chw;   // staged tape: lanes past H work on a valid address and store nothing
     const int t0 = blockIdx.z;
     const E* bxi = a.bx + (int64_t)i * a.bx_sn + (int64_t)ch0 * a.bx_sh;
     auto load_bx = [&](int t, float* x) {
@@ -170,13 +174,24 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const Con
         y[c] = conv;
     }
     E* q = a.out + (int64_t)i * a.out_sn + (int64_t)ch0 * a.out_sh + (int64_t)t0 * a.out_st;
-    if constexpr (VEC) {
-        store_f32x8s<E, LFM2SC_CVU_NT>(q, y);
-    } else {
+    if (on) {
+        if constexpr (VEC) {
+            store_f32x8s<E, LFM2SC_CVU_NT>(q, y);
+        } else {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
+            for (int c = 0; c < 8; ++c) st1<E>(q + (int64_t)c * a.out_sh, y[c]);
+        }
     }
-    store_block_s<E, K, (LFM2SC_CVU_NT & 8) ? 2 : 0>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
+    if constexpr (LFM2SC_CVU_STAGE != 0) {
+        // the wave's tape block of this step through LDS: contiguous 1 KiB per store instruction
+        __shared__ StateStage<E, K> stage;
+        const int nch = a.H - chw < kSmallBlock * kChPerLane ? a.H - chw : kSmallBlock * kChPerLane;
+        const rsrc_t blk = row_rsrc(a.win + (((int64_t)i * a.L + t0) * a.H + chw) * K,
+                                    (uint32_t)nch * K * (uint32_t)sizeof(E));
+        stage_store<E, K, (LFM2SC_CVU_NT & 8) ? kPolicyNt : 0>(stage, blk, lane, s);
+    } else {
+        store_block_s<E, K, (LFM2SC_CVU_NT & 8) ? 2 : 0>(a.win + (((int64_t)i * a.L + t0) * a.H + ch0) * K, s);
+    }
 }
 
 // Token stride 1: one lane per channel, all L steps of the sequence in the

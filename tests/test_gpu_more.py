@@ -198,6 +198,29 @@ def test_decode_batches_staging_states(K, dtype, H):
     assert_bits(g.pool, expect, "pool: valid slots advanced, every other slot untouched")
 
 
+def test_decode_staged_padded_pool():
+    """Staged decode (600 sequences) on a pool whose slots are padded apart (slot stride H*K + 72 elements):
+    the slot blocks are advanced bit for bit and the padding between them stays untouched."""
+    _say("case: staged decode, padded pool")
+    N, slots, H, K = 600, 650, 2048, 3
+    c = wl.decode_lfm2(seed=133, N=N, slots=slots, H=H, K=K)
+    stride = H * K + 72
+    big = torch.full((slots, stride), float("nan"), dtype=c.dtype)
+    big[:, :H * K] = c.pool.reshape(slots, H * K)
+    gbig = big.to(DEV)
+    pool = torch.as_strided(gbig, (slots, H, K), (stride, K, 1))
+    g = c.to(DEV)
+    y = _nan((N, H), c.dtype)
+    lfm2sc_decode_step(g.inp, g.w, pool, g.slot_idx, y)
+    torch.cuda.synchronize()
+    y_ref, p_ref = oracle.decode(c.inp, c.w, c.pool, c.slot_idx)
+    assert_close(y, y_ref, c.dtype, "y")
+    expect = big.clone()
+    used = c.slot_idx.long()
+    expect[used, :H * K] = rounded(p_ref[used.numpy()], c.dtype).reshape(len(used), H * K)
+    assert_bits(gbig, expect, "padded pool: slots advanced, padding untouched")
+
+
 def test_graph_capture_replays_match_eager():
     """Prefill + backward + decode captured in one HIP graph; each replay (with eager work and syncs in
     between) must reproduce the eager results bitwise."""
