@@ -203,8 +203,19 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_step_kernel(const Con
 template <typename E, int K, bool VEC>
 __global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const ConvUpdateArgs<E> a) {
     const int i = blockIdx.x;
-    const int ch = blockIdx.y * kSmallBlock + threadIdx.x;
-    if (ch >= a.H) return;
+    const int lane = (int)threadIdx.x;
+    const int chw = blockIdx.y * kSmallBlock;   // the wave's first channel
+    const bool staged = LFM2SC_CVU_STAGE != 0 && a.win != nullptr;
+    int ch = chw + lane;
+    const bool on = ch < a.H;
+    if (!staged && !on) return;
+    if (!on) ch = chw;   // staged tape: lanes past H work on a valid address and store nothing
+    // Staged tape: the wave's 64 channels x K of up to 8 steps go to LDS, then out
+    // as 16-byte pieces of each step's contiguous block.
+    __shared__ __align__(16) E stg[8 * kSmallBlock * K];
+    constexpr int kPiecesPerStep = kSmallBlock * K * (int)sizeof(E) / 16;
+    const int nch = a.H - chw < kSmallBlock ? a.H - chw : kSmallBlock;
+    const int step_pieces = nch * K * (int)sizeof(E) / 16;   // nch is a multiple of 8: whole pieces
     const int64_t slot = a.slot_idx[i];
     const bool ok = slot_ok(slot, a.num_slots);
     float w[K], s[K];
@@ -235,19 +246,40 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const Con
 #pragma unroll
                 for (int k = 0; k < K - 1; ++k) conv = fmaf(w[k], s[k], conv);
                 y[u] = conv;
-                if (a.win != nullptr) {
+                if (staged) {
+#pragma unroll
+                    for (int k = 0; k < K; ++k) st1<E>(&stg[(u * kSmallBlock + lane) * K + k], s[k]);
+                } else if (a.win != nullptr) {
                     E* wp = a.win + (((int64_t)i * a.L + t0 + u) * a.H + ch) * K;
 #pragma unroll
                     for (int k = 0; k < K; ++k) st1<E>(wp + k, s[k]);
                 }
             }
         }
-        if constexpr (VEC) {
-            store_f32x8s<E, LFM2SC_CVU_NT>(ob + t0, y);
-        } else {
+        if (staged) {
+            __syncthreads();
+            const uint4* src = reinterpret_cast<const uint4*>(stg);
+            for (int j = lane; j < n * kPiecesPerStep; j += kSmallBlock) {
+                const int u = j / kPiecesPerStep, piece = j % kPiecesPerStep;
+                if (piece < step_pieces) {
+                    E* wp = a.win + (((int64_t)i * a.L + t0 + u) * a.H + chw) * K;
+                    const uint4 v = src[j];
+                    u32x4* dst = reinterpret_cast<u32x4*>(wp) + piece;
+                    const u32x4 w = {v.x, v.y, v.z, v.w};
+                    if constexpr ((LFM2SC_CVU_NT & 8) != 0) __builtin_nontemporal_store(w, dst);
+                    else *dst = w;
+                }
+            }
+            __syncthreads();   // LDS free for the next 8 steps
+        }
+        if (on) {
+            if constexpr (VEC) {
+                store_f32x8s<E, LFM2SC_CVU_NT>(ob + t0, y);
+            } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (u < n) st1<E>(ob + t0 + u, y[u]);
+                for (int u = 0; u < 8; ++u)
+                    if (u < n) st1<E>(ob + t0 + u, y[u]);
+            }
         }
     }
     if (a.win == nullptr && ok) {
