@@ -10,8 +10,8 @@ import torch
 import oracle
 from gated_short_causal_amd import workloads as wl
 from gated_short_causal_amd import (Lfm2scError, lfm2sc_backward, lfm2sc_backward_workspace_bytes,
-                                    lfm2sc_commit_window, lfm2sc_decode_step, lfm2sc_prefill_ragged,
-                                    lfm2sc_verify_window)
+                                    lfm2sc_commit_window, lfm2sc_conv_update, lfm2sc_decode_step,
+                                    lfm2sc_prefill_ragged, lfm2sc_verify_window)
 from tests.parity_util import assert_bits, assert_close, rounded
 
 pytestmark = pytest.mark.gpu
@@ -266,6 +266,56 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for name, a, b in zip(("y", "d_in", "dW", "decode y", "pool"), (y, d_in, dW, yd, g.pool), ref):
             assert_bits(a, b, f"replay {rep}: {name}")
+
+
+def test_graph_capture_staged_small_calls():
+    """The small calls whose state or tape blocks go through LDS -- a 600-sequence decode, a verify window and
+    a verify-shaped conv update on the transposed view -- captured in one graph; every replay (with eager work
+    and syncs in between) reproduces the eager results bitwise."""
+    _say("case: graph capture, staged small calls")
+    H, K, N, L = 2048, 3, 600, 4
+    d = wl.decode_lfm2(seed=141, N=N, slots=N + 40, H=H, K=K).to(DEV)
+    v = wl.verify_lfm2(seed=142, N=48, L=L, slots=64, H=H, K=K).to(DEV)
+    dpool0, vpool0 = d.pool.clone(), v.pool.clone()
+    yd = torch.empty(N, H, dtype=d.dtype, device=DEV)
+    yv = torch.empty(48 * L, H, dtype=v.dtype, device=DEV)
+    win = torch.empty(48, L, H, K, dtype=v.dtype, device=DEV)
+    bx = v.inp[:, :H].contiguous().view(48, L, H).transpose(1, 2)
+    out = torch.empty(48, L, H, dtype=v.dtype, device=DEV).transpose(1, 2)
+    tape = torch.empty(48, L, H, K, dtype=v.dtype, device=DEV)
+
+    def step():
+        lfm2sc_decode_step(d.inp, d.w, d.pool, d.slot_idx, yd)
+        lfm2sc_verify_window(v.inp, v.w, v.pool, v.slot_idx, L, win, yv)
+        lfm2sc_conv_update(bx, v.w, v.pool, v.slot_idx, out, windows=tape)
+
+    step()
+    torch.cuda.synchronize()
+    outs = (yd, d.pool, yv, win, out, tape)
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        d.pool.copy_(dpool0)
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    d.pool.copy_(dpool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (yd, yv, win, out, tape):
+            t.fill_(float("nan"))
+        d.pool.copy_(dpool0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("decode y", "decode pool", "verify y", "verify tape", "conv update out",
+                               "conv update tape"), outs, ref):
+            assert_bits(a, b, f"replay {rep}: {name}")
+    assert_bits(v.pool, vpool0, "verify and the tape-mode conv update leave the pool untouched")
 
 
 _CHECK_SCRIPT = r"""
