@@ -265,9 +265,9 @@ __global__ __launch_bounds__(kSmallBlock) void conv_update_rows_kernel(const Con
                     E* wp = a.win + (((int64_t)i * a.L + t0 + u) * a.H + chw) * K;
                     const uint4 v = src[j];
                     u32x4* dst = reinterpret_cast<u32x4*>(wp) + piece;
-                    const u32x4 w = {v.x, v.y, v.z, v.w};
-                    if constexpr ((LFM2SC_CVU_NT & 8) != 0) __builtin_nontemporal_store(w, dst);
-                    else *dst = w;
+                    const u32x4 pv = {v.x, v.y, v.z, v.w};
+                    if constexpr ((LFM2SC_CVU_NT & 8) != 0) __builtin_nontemporal_store(pv, dst);
+                    else *dst = pv;
                 }
             }
             __syncthreads();   // LDS free for the next 8 steps
