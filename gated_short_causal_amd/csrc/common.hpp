@@ -33,6 +33,9 @@
 #ifndef LFM2SC_FWD_TW
 #define LFM2SC_FWD_TW 4        // forward workgroup: waves along time (4: 4 consecutive windows of one 512-channel
 #endif                         // group; 1: one window across 4 x 512 channels)
+#ifndef LFM2SC_FWD_TW_RAGGED
+#define LFM2SC_FWD_TW_RAGGED 1 // the same for forward calls of more than one sequence
+#endif
 #ifndef LFM2SC_BWD_TW
 #define LFM2SC_BWD_TW 4        // same for the backward
 #endif

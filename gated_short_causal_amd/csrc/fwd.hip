@@ -50,16 +50,16 @@ __device__ __forceinline__ void fwd_token(const Raw8<E>& rb, const Raw8<E>& rc, 
 // only ones that see the initial state) and writes the final state, which it
 // forms from the slot (for entries the sequence does not overwrite) and the
 // B, xv rows of the sequence's last K tokens.  No other wave touches the slot.
-template <typename E, int K, int U>
+template <typename E, int K, int U, int TW>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs<E> a) {
-    using Lay = WgLayout<LFM2SC_FWD_TW>;
+    using Lay = WgLayout<TW>;
     const int wave = wave_id();
     const int lane = threadIdx.x % kWave;
     const int tile = xcd_tile(blockIdx.x, gridDim.x);
     if (tile >= a.ntiles) return;
-    const int ch0 = ((blockIdx.y * Lay::kCW + wave / LFM2SC_FWD_TW) * kWave + lane) * kChPerLane;
-    const int64_t gap = (int64_t)a.sub * LFM2SC_FWD_TW;
-    const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % LFM2SC_FWD_TW) * a.sub;
+    const int ch0 = ((blockIdx.y * Lay::kCW + wave / TW) * kWave + lane) * kChPerLane;
+    const int64_t gap = (int64_t)a.sub * TW;
+    const int64_t v0 = (int64_t)tile * gap + (int64_t)(wave % TW) * a.sub;
     SeqSpan sp;
     if (!find_span(a.cu, a.N, a.total_T, gap, v0, v0 + a.sub, sp)) return;   // all lanes still active here
     if (ch0 >= a.H) return;
@@ -477,19 +477,32 @@ int64_t ragged_tiles_bound(int64_t total_T, int N) {
 // for bf16 (6.1 TB/s; 12 rows: 5.9) and 2 for fp32 (5.1 TB/s; 12 rows: 4.8).
 template <typename E> constexpr int fwd_unroll() { return sizeof(E) == 4 ? LFM2SC_FWD_U_F32 : LFM2SC_FWD_U; }
 
-template <typename E, int K>
-static hipError_t prefill_k(PrefillArgs<E> a, hipStream_t s) {
-    constexpr auto kernel = prefill_kernel<E, K, fwd_unroll<E>()>;
+template <typename E, int K, int TW>
+static hipError_t prefill_tw(PrefillArgs<E> a, hipStream_t s) {
+    constexpr auto kernel = prefill_kernel<E, K, fwd_unroll<E>(), TW>;
     static const int resident_long = resident_workgroups(kernel, LFM2SC_FWD_LDS);
     static const int resident_short = resident_workgroups(kernel, 0);
     const bool short_call = a.total_T < LFM2SC_SHORT_T;
-    const int gy = WgLayout<LFM2SC_FWD_TW>::groups(a.H);
-    const Tiling t = ragged_tiling(a.total_T, a.N, gy, short_call ? resident_short : resident_long, LFM2SC_FWD_TW,
+    const int gy = WgLayout<TW>::groups(a.H);
+    const Tiling t = ragged_tiling(a.total_T, a.N, gy, short_call ? resident_short : resident_long, TW,
                                    (int64_t)a.H * (int64_t)sizeof(E), kWinSpanFwd);
     a.sub = t.sub;
     a.ntiles = (int)t.ntiles;
     hipLaunchKernelGGL(kernel, dim3(pad_xcd(a.ntiles), gy), dim3(kThreads), short_call ? 0 : LFM2SC_FWD_LDS, s, a);
     return hipGetLastError();
+}
+
+// One sequence: workgroups of LFM2SC_FWD_TW consecutive windows of one
+// 512-channel group.  Several: one window per workgroup across 4 channel
+// groups, so the gap the virtual axis leaves between two sequences is one
+// window instead of LFM2SC_FWD_TW (with 8 sequences the gaps took 7 of 64
+// window slots per channel group; measured ragged prefill of 8 sequences,
+// ~7,000 tokens: 27.7 -> 26.9 us per call; a single 65,536-token sequence
+// is 1% slower that way, 200 vs 202 us).
+template <typename E, int K>
+static hipError_t prefill_k(PrefillArgs<E> a, hipStream_t s) {
+    if (a.N > 1 && LFM2SC_FWD_TW_RAGGED != LFM2SC_FWD_TW) return prefill_tw<E, K, LFM2SC_FWD_TW_RAGGED>(a, s);
+    return prefill_tw<E, K, LFM2SC_FWD_TW>(a, s);
 }
 
 template <typename E>
